@@ -1,0 +1,121 @@
+"""Torch-tensor wrappers of the C ABI.  Marshalling only: shapes and pointers in,
+status codes checked; outputs and workspaces are allocated with torch when the
+caller does not pass them."""
+import ctypes
+
+import torch
+
+from . import _lib as L
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ws(nbytes, device, ws):
+    if nbytes == 0:
+        return None, 0
+    if ws is not None:
+        return ws, ws.numel() * ws.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def indexer_scores(q, k, w, *, q_scale=None, k_scale=None, q_pos0=0, row0=0, rows=None, out=None):
+    """Materialised indexer scores [B, rows, n_k] fp32 (-inf where s > t)."""
+    B, n_q = q.shape[:2]
+    rows = n_q - row0 if rows is None else rows
+    if out is None:
+        out = torch.empty((B, rows, k.shape[1]), dtype=torch.float32, device=q.device)
+    a = L.indexer_args(q, k, w, q_scale, k_scale, q_pos0)
+    L.check(L.dsa_indexer_scores(ctypes.byref(a), row0, rows, out.data_ptr(), _stream()))
+    return out
+
+
+def topk_workspace_size(q, k, w, topk, *, q_scale=None, k_scale=None, q_pos0=0, scores=None):
+    a = L.indexer_args(q, k, w, q_scale, k_scale, q_pos0)
+    return L.dsa_topk_workspace_size(ctypes.byref(a), None if scores is None else scores.data_ptr(), topk)
+
+
+def topk(q, k, w, topk, *, q_scale=None, k_scale=None, q_pos0=0, scores=None, out=None, ws=None):
+    """INDEXER + Top-k (scores=None) or Top-k over given scores [B, n_q, n_k].
+    Returns int32 [B, n_q, topk], ascending rows with -1 padding."""
+    B, n_q = q.shape[:2]
+    if out is None:
+        out = torch.empty((B, n_q, topk), dtype=torch.int32, device=q.device)
+    a = L.indexer_args(q, k, w, q_scale, k_scale, q_pos0)
+    sp = None if scores is None else scores.data_ptr()
+    need = L.dsa_topk_workspace_size(ctypes.byref(a), sp, topk)
+    wbuf, wbytes = _ws(need, q.device, ws)
+    L.check(L.dsa_topk(ctypes.byref(a), sp, topk, out.data_ptr(), None if wbuf is None else wbuf.data_ptr(),
+                       wbytes, _stream()))
+    return out
+
+
+def sparse_attn_workspace_size(q, kv, idx, d_v, *, v=None):
+    dummy = torch.empty(0)
+    a = L.sparse_attn_args(q, kv, idx, 1.0, dummy, v=v, d_v=d_v)
+    return L.dsa_sparse_attn_workspace_size(ctypes.byref(a))
+
+
+def sparse_attn(q, kv, idx, scale, *, d_v=None, v=None, out=None, ws=None):
+    """Sparse attention; returns fp32 [B, n_q, H, d_v]."""
+    B, n_q, H, _ = q.shape
+    if d_v is None:
+        d_v = v.shape[-1] if v is not None else kv.shape[-1]
+    if out is None:
+        out = torch.empty((B, n_q, H, d_v), dtype=torch.float32, device=q.device)
+    a = L.sparse_attn_args(q, kv, idx, scale, out, v=v, d_v=d_v)
+    need = L.dsa_sparse_attn_workspace_size(ctypes.byref(a))
+    wbuf, wbytes = _ws(need, q.device, ws)
+    L.check(L.dsa_sparse_attn(ctypes.byref(a), None if wbuf is None else wbuf.data_ptr(), wbytes, _stream()))
+    return out
+
+
+def _layers(specs, k):
+    arr = (L.Layer * len(specs))()
+    for i, s in enumerate(specs):
+        ix = s.get("ix")
+        if ix is not None:
+            arr[i].ix = L.indexer_args(ix["q"], ix["k"], ix["w"], ix.get("q_scale"), ix.get("k_scale"),
+                                       ix.get("q_pos0", 0))
+        sa = s["sa"]
+        arr[i].sa = L.sparse_attn_args(sa["q"], sa["kv"], None, sa["scale"], sa["out"], v=sa.get("v"),
+                                       d_v=sa.get("d_v"))
+        arr[i].sa.topk = k
+        io = s.get("idx_out")
+        arr[i].idx_out = None if io is None else io.data_ptr()
+    return arr
+
+
+def indexcache_forward_workspace_size(pattern, specs, k):
+    arr = _layers(specs, k)
+    return L.indexcache_forward_workspace_size(pattern.encode(), len(specs), arr, k)
+
+
+def indexcache_forward(pattern, specs, k, *, ws=None):
+    """IndexCache loop.  specs[l] = {"ix": {...} (F layers only), "sa": {"q", "kv", "scale", "out",
+    optional "v", "d_v"}, "idx_out": int32 tensor (F layers only)}.  Returns the 0-based source layer
+    of every layer's index tensor."""
+    arr = _layers(specs, k)
+    n = len(specs)
+    need = L.indexcache_forward_workspace_size(pattern.encode(), n, arr, k)
+    dev = specs[0]["sa"]["q"].device
+    wbuf, wbytes = _ws(need, dev, ws)
+    src = (ctypes.c_int32 * n)()
+    L.check(L.indexcache_forward_c(pattern.encode(), n, arr, k, src,
+                                   None if wbuf is None else wbuf.data_ptr(), wbytes, _stream()))
+    return list(src)
+
+
+def index_overlap(a, b, k, *, rows=None, row_counts=None, total=None):
+    """Adds sum_r |a[r] ∩ b[r]| to `total` (uint64 stored in an int64 tensor of one element);
+    optionally writes per-row counts.  a, b: int32 [rows, k] (any leading dims flattened)."""
+    a2 = a.reshape(-1, k)
+    b2 = b.reshape(-1, k)
+    rows = a2.shape[0] if rows is None else rows
+    if total is None:
+        total = torch.zeros(1, dtype=torch.int64, device=a.device)
+    L.check(L.dsa_index_overlap(a2.data_ptr(), b2.data_ptr(), rows, k,
+                                None if row_counts is None else row_counts.data_ptr(),
+                                total.data_ptr(), _stream()))
+    return total

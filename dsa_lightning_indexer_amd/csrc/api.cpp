@@ -1,0 +1,330 @@
+// C ABI: argument validation, workspace sizing, kernel dispatch and the
+// IndexCache F/S layer loop ([IC-SUMMARY] Algorithm (b); [DSA-NOTES] §2.2).
+// Every check runs before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "common.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dsa_status fail(dsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+dsa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DSA_OK;
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// ------------------------------------------------------------------ indexer args
+dsa_status check_indexer_shape(const dsa_indexer_args* a) {
+  if (!a) return fail(DSA_ERR_INVALID, "indexer args is NULL");
+  if (a->dtype != DSA_F32 && a->dtype != DSA_BF16 && a->dtype != DSA_FP8_E4M3)
+    return fail(DSA_ERR_INVALID, "unknown indexer dtype %d", a->dtype);
+  if (a->batch < 1 || a->n_q < 1 || a->n_k < 1)
+    return fail(DSA_ERR_INVALID, "batch, n_q and n_k must be >= 1 (got %d, %d, %d)", a->batch,
+                a->n_q, a->n_k);
+  if (a->q_pos0 < 0) return fail(DSA_ERR_INVALID, "q_pos0 must be >= 0");
+  if (a->heads < 1 || a->heads > DSA_MAX_INDEXER_HEADS)
+    return fail(DSA_ERR_UNSUPPORTED, "indexer heads must be 1..%d (got %d)", DSA_MAX_INDEXER_HEADS,
+                a->heads);
+  if (a->dtype == DSA_F32) {
+    if (a->dim < 1 || a->dim > 256 || a->heads * a->dim > 8192)
+      return fail(DSA_ERR_UNSUPPORTED, "F32 indexer needs dim 1..256 and heads*dim <= 8192");
+    if (a->n_q > 65535 || a->batch > 65535)
+      return fail(DSA_ERR_UNSUPPORTED, "F32 indexer needs n_q and batch <= 65535");
+  } else if (!dsa_host::indexer_mfma_supported(*a)) {
+    return fail(DSA_ERR_UNSUPPORTED, "indexer dim %d unsupported for dtype %d (bf16: 32/64/128, fp8: 64/128)",
+                a->dim, a->dtype);
+  }
+  if (a->k_batch_stride != 0 && a->k_batch_stride < (int64_t)a->n_k * a->dim)
+    return fail(DSA_ERR_INVALID, "k_batch_stride smaller than n_k*dim");
+  if (a->k_scale_batch_stride != 0 && a->k_scale_batch_stride < a->n_k)
+    return fail(DSA_ERR_INVALID, "k_scale_batch_stride smaller than n_k");
+  return DSA_OK;
+}
+
+dsa_status check_indexer_data(const dsa_indexer_args* a) {
+  if (!a->q || !a->k || !a->w) return fail(DSA_ERR_INVALID, "indexer q, k and w must be non-NULL");
+  if (a->dtype == DSA_FP8_E4M3 && (!a->q_scale || !a->k_scale))
+    return fail(DSA_ERR_INVALID, "fp8 indexer needs q_scale and k_scale");
+  const size_t al = a->dtype == DSA_F32 ? 4 : 16;
+  if (!aligned(a->q, al) || !aligned(a->k, al) || !aligned(a->w, 4))
+    return fail(DSA_ERR_INVALID, "indexer q/k must be %zu-byte aligned, w 4-byte aligned", al);
+  if (a->dtype != DSA_F32 && a->k_batch_stride != 0 &&
+      (a->k_batch_stride * (a->dtype == DSA_BF16 ? 2 : 1)) % 16 != 0)
+    return fail(DSA_ERR_INVALID, "k batch stride must keep 16-byte row alignment");
+  return DSA_OK;
+}
+
+bool decode_shaped(const dsa_indexer_args* a) {
+  return (int64_t)a->batch * a->n_q <= 256 && a->n_k > 2048;
+}
+
+enum TopkPath { PATH_SELECT, PATH_F32, PATH_FUSED, PATH_SCAN };
+
+TopkPath topk_path(const dsa_indexer_args* a, const float* scores) {
+  if (scores) return PATH_SELECT;
+  if (a->dtype == DSA_F32) return PATH_F32;
+  return decode_shaped(a) ? PATH_SCAN : PATH_FUSED;
+}
+
+size_t topk_ws(const dsa_indexer_args* a, const float* scores) {
+  const int64_t rows = (int64_t)a->batch * a->n_q;
+  switch (topk_path(a, scores)) {
+    case PATH_SELECT: return align_up(dsa_host::select_workspace_bytes(rows));
+    case PATH_F32:
+    case PATH_SCAN:
+      return align_up((size_t)rows * a->n_k * sizeof(float)) +
+             align_up(dsa_host::select_workspace_bytes(rows));
+    case PATH_FUSED: return 0;
+  }
+  return 0;
+}
+
+dsa_status check_topk(const dsa_indexer_args* a, const float* scores, int32_t k, const int32_t* idx,
+                      const void* ws, size_t ws_bytes) {
+  dsa_status st = check_indexer_shape(a);
+  if (st != DSA_OK) return st;
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID, "k must be 1..%d (got %d)", DSA_MAX_TOPK, k);
+  if (!idx) return fail(DSA_ERR_INVALID, "idx is NULL");
+  if (!aligned(idx, 4)) return fail(DSA_ERR_INVALID, "idx must be 4-byte aligned");
+  if (scores) {
+    if (!aligned(scores, 4)) return fail(DSA_ERR_INVALID, "scores must be 4-byte aligned");
+  } else {
+    st = check_indexer_data(a);
+    if (st != DSA_OK) return st;
+  }
+  const size_t need = topk_ws(a, scores);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
+  if (ws && !aligned(ws, kAlign)) return fail(DSA_ERR_INVALID, "workspace must be 256-byte aligned");
+  return DSA_OK;
+}
+
+dsa_status run_topk(const dsa_indexer_args* a, const float* scores, int32_t k, int32_t* idx, void* ws,
+                    hipStream_t s) {
+  const int64_t rows = (int64_t)a->batch * a->n_q;
+  dsa_host::SelectPlan plan{rows, a->n_q, a->q_pos0, a->n_k, k, (int64_t)a->n_k};
+  const TopkPath path = topk_path(a, scores);
+  hipError_t e = hipSuccess;
+  if (path == PATH_FUSED) {
+    e = dsa_host::indexer_topk_fused(*a, k, idx, s);
+    return hip_status(e, "fused indexer+topk launch");
+  }
+  const float* sc = scores;
+  void* sel_ws = ws;
+  if (path == PATH_F32 || path == PATH_SCAN) {
+    float* buf = (float*)ws;
+    sel_ws = (char*)ws + align_up((size_t)rows * a->n_k * sizeof(float));
+    if (path == PATH_F32) {
+      e = dsa_host::indexer_scores_f32(*a, 0, a->n_q, buf, a->n_k, s);
+    } else {
+      e = dsa_host::indexer_scan(*a, buf, sel_ws, k, s);
+    }
+    if (e != hipSuccess) return hip_status(e, "indexer scoring launch");
+    sc = buf;
+  }
+  e = dsa_host::select_prepare(sel_ws, rows, s);
+  if (e == hipSuccess) e = dsa_host::select_hist1(sc, plan, sel_ws, s);
+  if (e == hipSuccess) e = dsa_host::select_finish(sc, plan, sel_ws, idx, s);
+  return hip_status(e, "top-k select launch");
+}
+
+// ------------------------------------------------------------------ attention args
+dsa_status check_sa(const dsa_sparse_attn_args* a, bool need_idx) {
+  if (!a) return fail(DSA_ERR_INVALID, "sparse attention args is NULL");
+  if (a->dtype != DSA_F32 && a->dtype != DSA_BF16)
+    return fail(DSA_ERR_UNSUPPORTED, "sparse attention dtype must be F32 or BF16 (got %d)", a->dtype);
+  if (a->batch < 1 || a->n_q < 1 || a->n_k < 1 || a->heads < 1 || a->kv_heads < 1)
+    return fail(DSA_ERR_INVALID, "sparse attention sizes must be >= 1");
+  if (a->heads % a->kv_heads) return fail(DSA_ERR_INVALID, "heads must be a multiple of kv_heads");
+  if (a->d_qk < 1 || a->d_qk > 1024 || a->d_v < 1 || a->d_v > 1024)
+    return fail(DSA_ERR_UNSUPPORTED, "d_qk and d_v must be 1..1024");
+  if (!a->v && a->d_v > a->d_qk) return fail(DSA_ERR_INVALID, "latent V needs d_v <= d_qk");
+  if (a->topk < 1 || a->topk > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID, "topk must be 1..%d", DSA_MAX_TOPK);
+  if (!a->q || !a->kv || !a->out || (need_idx && !a->idx))
+    return fail(DSA_ERR_INVALID, "sparse attention q, kv, idx and out must be non-NULL");
+  if (!(a->scale == a->scale)) return fail(DSA_ERR_INVALID, "scale is NaN");
+  const int64_t row = (int64_t)a->kv_heads * a->d_qk;
+  if (a->kv_batch_stride != 0 && a->kv_batch_stride < (int64_t)a->n_k * row)
+    return fail(DSA_ERR_INVALID, "kv_batch_stride too small");
+  if (a->v && a->v_batch_stride != 0 && a->v_batch_stride < (int64_t)a->n_k * a->kv_heads * a->d_v)
+    return fail(DSA_ERR_INVALID, "v_batch_stride too small");
+  const size_t al = a->dtype == DSA_BF16 ? 16 : 4;
+  if (!aligned(a->q, al) || !aligned(a->kv, al) || !aligned(a->out, 4) ||
+      (a->idx && !aligned(a->idx, 4)) || (a->v && !aligned(a->v, 4)))
+    return fail(DSA_ERR_INVALID, "sparse attention pointers misaligned");
+  if (a->dtype == DSA_BF16 && a->kv_batch_stride % 8 != 0)
+    return fail(DSA_ERR_INVALID, "bf16 kv batch stride must keep 16-byte alignment");
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char* dsa_status_string(int32_t st) {
+  switch (st) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_INVALID: return "invalid argument";
+    case DSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case DSA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* dsa_last_error(void) { return g_last_error.c_str(); }
+
+dsa_status dsa_indexer_scores(const dsa_indexer_args* a, int64_t row0, int64_t rows, float* scores,
+                              hipStream_t stream) {
+  g_last_error.clear();
+  dsa_status st = check_indexer_shape(a);
+  if (st != DSA_OK) return st;
+  st = check_indexer_data(a);
+  if (st != DSA_OK) return st;
+  if (!scores || !aligned(scores, 4)) return fail(DSA_ERR_INVALID, "scores must be non-NULL and 4-byte aligned");
+  if (row0 < 0 || rows < 1 || row0 + rows > a->n_q)
+    return fail(DSA_ERR_INVALID, "row window [%lld, %lld) outside [0, %d)", (long long)row0,
+                (long long)(row0 + rows), a->n_q);
+  hipError_t e = a->dtype == DSA_F32
+                     ? dsa_host::indexer_scores_f32(*a, row0, rows, scores, a->n_k, stream)
+                     : dsa_host::indexer_scores_mfma(*a, row0, rows, scores, stream);
+  return hip_status(e, "indexer scores launch");
+}
+
+size_t dsa_topk_workspace_size(const dsa_indexer_args* a, const float* scores, int32_t k) {
+  (void)k;
+  if (!a || check_indexer_shape(a) != DSA_OK) return 0;
+  return topk_ws(a, scores);
+}
+
+dsa_status dsa_topk(const dsa_indexer_args* a, const float* scores, int32_t k, int32_t* idx, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  dsa_status st = check_topk(a, scores, k, idx, ws, ws_bytes);
+  if (st != DSA_OK) return st;
+  return run_topk(a, scores, k, idx, ws, stream);
+}
+
+size_t dsa_sparse_attn_workspace_size(const dsa_sparse_attn_args* a) {
+  if (!a || check_sa(a, false) != DSA_OK) return 0;
+  return align_up(dsa_host::sparse_attn_ws_bytes(*a));
+}
+
+dsa_status dsa_sparse_attn(const dsa_sparse_attn_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  dsa_status st = check_sa(a, true);
+  if (st != DSA_OK) return st;
+  const size_t need = dsa_host::sparse_attn_ws_bytes(*a);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
+  if (ws && !aligned(ws, kAlign)) return fail(DSA_ERR_INVALID, "workspace must be 256-byte aligned");
+  return hip_status(dsa_host::sparse_attn_launch(*a, ws, stream), "sparse attention launch");
+}
+
+static dsa_status check_forward(const char* pattern, int32_t n, const dsa_layer* layers, int32_t k,
+                                size_t* ws_need) {
+  if (!pattern) return fail(DSA_ERR_INVALID, "pattern is NULL");
+  if (n < 1) return fail(DSA_ERR_INVALID, "n_layers must be >= 1");
+  if ((int64_t)strnlen(pattern, (size_t)n + 1) != n)
+    return fail(DSA_ERR_INVALID, "pattern length differs from n_layers=%d", n);
+  for (int32_t l = 0; l < n; ++l)
+    if (pattern[l] != 'F' && pattern[l] != 'S')
+      return fail(DSA_ERR_INVALID, "pattern[%d]='%c' is neither F nor S", l, pattern[l]);
+  if (pattern[0] != 'F') return fail(DSA_ERR_INVALID, "the first layer must be F");
+  if (!layers) return fail(DSA_ERR_INVALID, "layers is NULL");
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID, "k must be 1..%d", DSA_MAX_TOPK);
+  size_t need = 0;
+  int32_t src = -1;
+  for (int32_t l = 0; l < n; ++l) {
+    const dsa_layer& L = layers[l];
+    if (pattern[l] == 'F') {
+      src = l;
+      dsa_status st = check_indexer_shape(&L.ix);
+      if (st == DSA_OK) st = check_indexer_data(&L.ix);
+      if (st != DSA_OK) return fail(st, "layer %d (F): %s", l, g_last_error.c_str());
+      if (!L.idx_out || !aligned(L.idx_out, 4)) return fail(DSA_ERR_INVALID, "layer %d (F): idx_out NULL/misaligned", l);
+      const size_t w = topk_ws(&L.ix, nullptr);
+      if (w > need) need = w;
+    }
+    dsa_status st = check_sa(&L.sa, false);
+    if (st != DSA_OK) return fail(st, "layer %d: %s", l, g_last_error.c_str());
+    const dsa_indexer_args& S = layers[src].ix;
+    if (L.sa.batch != S.batch || L.sa.n_q != S.n_q || L.sa.topk != k)
+      return fail(DSA_ERR_INVALID, "layer %d: attention batch/n_q/topk (%d,%d,%d) must match the cached "
+                  "index tensor (%d,%d,%d)", l, L.sa.batch, L.sa.n_q, L.sa.topk, S.batch, S.n_q, k);
+    const size_t w = align_up(dsa_host::sparse_attn_ws_bytes(L.sa));
+    if (w > need) need = w;
+  }
+  *ws_need = need;
+  return DSA_OK;
+}
+
+size_t indexcache_forward_workspace_size(const char* pattern, int32_t n, const dsa_layer* layers, int32_t k) {
+  size_t need = 0;
+  if (check_forward(pattern, n, layers, k, &need) != DSA_OK) return 0;
+  return need;
+}
+
+dsa_status indexcache_forward(const char* pattern, int32_t n, const dsa_layer* layers, int32_t k,
+                              int32_t* src_layer, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  size_t need = 0;
+  dsa_status st = check_forward(pattern, n, layers, k, &need);
+  if (st != DSA_OK) return st;
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
+  if (ws && !aligned(ws, kAlign)) return fail(DSA_ERR_INVALID, "workspace must be 256-byte aligned");
+  const int32_t* cache = nullptr;   // the current index tensor (T_cache)
+  int32_t src = -1;
+  for (int32_t l = 0; l < n; ++l) {
+    const dsa_layer& L = layers[l];
+    if (pattern[l] == 'F') {
+      // F: INDEXER + Top-k; the result replaces the cached tensor.
+      st = run_topk(&L.ix, nullptr, k, L.idx_out, ws, stream);
+      if (st != DSA_OK) return st;
+      cache = L.idx_out;
+      src = l;
+    }
+    // S: reuse the cached tensor; no indexer launch, L.ix and L.idx_out untouched.
+    if (src_layer) src_layer[l] = src;
+    dsa_sparse_attn_args sa = L.sa;
+    sa.idx = cache;
+    st = hip_status(dsa_host::sparse_attn_launch(sa, ws, stream), "sparse attention launch");
+    if (st != DSA_OK) return st;
+  }
+  return DSA_OK;
+}
+
+dsa_status dsa_index_overlap(const int32_t* a, const int32_t* b, int64_t rows, int32_t k,
+                             int32_t* row_counts, unsigned long long* total, hipStream_t stream) {
+  g_last_error.clear();
+  if (rows < 0) return fail(DSA_ERR_INVALID, "rows must be >= 0");
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID, "k must be 1..%d", DSA_MAX_TOPK);
+  if (rows > 0 && (!a || !b)) return fail(DSA_ERR_INVALID, "index tensors must be non-NULL");
+  if (!row_counts && !total) return fail(DSA_ERR_INVALID, "need row_counts and/or total");
+  return hip_status(dsa_host::overlap_launch(a, b, rows, k, row_counts, total, stream), "overlap launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// Shared device/host helpers for the gfx950 kernels (wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dsa.h"
+
+namespace dsa {
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// Monotone map fp32 -> u32: a > b (as reals) iff key(a) > key(b).  Both zeros
+// map to the key of +0.0 so that -0.0 and +0.0 tie (and the lower position wins).
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t b = __float_as_uint(x);
+  b = (x == 0.0f) ? 0u : b;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// Lane-mask helpers (wave64).
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// Exclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t* total) {
+  const int lane = threadIdx.x & 63;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  *total = __shfl(x, 63, 64);
+  return x - v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace dsa
+
+// Host-side launch helpers (defined in the kernel translation units).
+namespace dsa_host {
+
+struct SelectPlan {
+  // rows are flattened (batch, n_q); row r has query position q_pos0 + r % n_q and
+  // candidates s = 0..min(t, n_k-1).
+  int64_t rows;
+  int32_t n_q;
+  int64_t q_pos0;
+  int32_t n_k;
+  int32_t k;
+  int64_t row_stride;  // elements between score rows
+};
+
+size_t select_workspace_bytes(int64_t rows);
+// Zero the select state (fill kernel; safe under stream capture).
+hipError_t select_prepare(void* ws, int64_t rows, hipStream_t s);
+// First histogram pass over materialised scores (skip if the producer fused it).
+hipError_t select_hist1(const float* scores, const SelectPlan& p, void* ws, hipStream_t s);
+// Remaining passes and the ordered write of idx [rows, k].
+hipError_t select_finish(const float* scores, const SelectPlan& p, void* ws, int32_t* idx,
+                         hipStream_t s);
+
+hipError_t indexer_scores_f32(const dsa_indexer_args& a, int64_t row0, int64_t rows, float* out,
+                              int64_t out_row_stride, hipStream_t s);
+hipError_t indexer_scores_mfma(const dsa_indexer_args& a, int64_t row0, int64_t rows, float* out,
+                               hipStream_t s);
+hipError_t indexer_topk_fused(const dsa_indexer_args& a, int32_t k, int32_t* idx, hipStream_t s);
+// Decode-shaped scan: fp32 scores of every (row, s) into `scores` [batch*n_q, n_k] and the
+// first select histogram into the select workspace `sel_ws` (already prepared).
+hipError_t indexer_scan(const dsa_indexer_args& a, float* scores, void* sel_ws, int32_t k,
+                        hipStream_t s);
+bool indexer_mfma_supported(const dsa_indexer_args& a);
+
+size_t sparse_attn_ws_bytes(const dsa_sparse_attn_args& a);
+hipError_t sparse_attn_launch(const dsa_sparse_attn_args& a, void* ws, hipStream_t s);
+
+hipError_t overlap_launch(const int32_t* a, const int32_t* b, int64_t rows, int32_t k,
+                          int32_t* row_counts, unsigned long long* total, hipStream_t s);
+
+}  // namespace dsa_host

@@ -1,0 +1,571 @@
+// Lightning-indexer kernels for gfx950 ([DSA-NOTES] §2.1 score equation):
+//     I[t, s] = sum_j w[t, j] * ReLU(q[t, j, :] . k[s, :]),  s = 0..t
+//
+//  * indexer_f32_kernel   fp32 inputs, plain VALU dot products (small/debug shapes).
+//  * ix_tile_kernel       bf16 / fp8-e4m3 inputs on MFMA.  One wave owns one query
+//    row: its q (heads x dim) stays in registers as the MFMA A operand (heads are
+//    the M dimension, 32 per tile), 64-key tiles of k are staged once per
+//    workgroup in LDS and read as the B operand.  The epilogue applies ReLU and
+//    the head weights in registers and reduces over heads inside each lane (the
+//    32x32 MFMA output puts 16 head rows of one key column in each lane), then
+//    across the two half-waves, leaving one score per lane per 64-key tile.
+//      MODE_SCORES writes the scores (debug / inspection path).
+//      MODE_TOPK never writes them: each wave keeps a candidate buffer in LDS,
+//      filtered by the running k-th key, compacted by a wave-level radix select
+//      when full.  Candidates arrive in position order and compaction is
+//      stable, so the kept set stays in ascending position order and ties are
+//      broken toward the lower position with no extra sort.
+//  * ix_scan_kernel       decode shape (few query rows, long key range): keys are
+//    split over many workgroups, B operands come straight from HBM in 128-byte
+//    rows, fp32 scores go to a workspace row for the multi-workgroup select.
+//
+// fp8: q = q_scale[t, j] * code, k = k_scale[s] * code with positive scales, so
+// w_j * ReLU(q_j . k) = k_scale[s] * (w_j * q_scale[t, j]) * ReLU(code_q . code_k):
+// the MFMA runs on raw e4m3 codes and both scales are applied in the epilogue.
+#include "common.hpp"
+
+namespace {
+
+using namespace dsa;
+
+enum { DT_BF16 = 1, DT_FP8 = 2 };
+enum { MODE_SCORES = 0, MODE_TOPK = 1 };
+
+constexpr int kTileKeys = 64;
+constexpr int kRowsPerBlock = 4;       // one query row per wave
+constexpr int kCandCap = 3072;         // per-row candidate buffer (>= k + 64)
+
+struct IxParams {
+  const void* q;
+  const float* q_scale;
+  const void* k;
+  int64_t k_bs;          // elements between batches of k
+  const float* k_scale;
+  int64_t ks_bs;
+  const float* w;
+  int32_t batch, n_q, n_k, heads;
+  int64_t q_pos0;
+  int64_t row0, rows;    // query rows handled (scores mode: a window)
+  float* out;            // scores [batch, rows, n_k]
+  int32_t* idx;          // [batch, n_q, topk]
+  int32_t topk;
+};
+
+// ---------------------------------------------------------------- fp32 path
+__global__ __launch_bounds__(256) void indexer_f32_kernel(IxParams p, int dim, int64_t out_rs) {
+  extern __shared__ float qs[];                 // heads * dim (+ heads weights)
+  const int64_t rr = blockIdx.y;                // row within the window
+  const int b = blockIdx.z;
+  const int64_t i = p.row0 + rr;
+  const int64_t t = p.q_pos0 + i;
+  const float* q = (const float*)p.q + ((int64_t)b * p.n_q + i) * p.heads * dim;
+  const float* w = p.w + ((int64_t)b * p.n_q + i) * p.heads;
+  float* wsh = qs + p.heads * dim;
+  for (int x = threadIdx.x; x < p.heads * dim; x += blockDim.x) qs[x] = q[x];
+  for (int x = threadIdx.x; x < p.heads; x += blockDim.x) wsh[x] = w[x];
+  __syncthreads();
+  const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= p.n_k) return;
+  float* out = p.out + ((int64_t)b * p.rows + rr) * out_rs;
+  if (s > t) { out[s] = -__builtin_inff(); return; }
+  const float* kr = (const float*)p.k + b * p.k_bs + s * dim;
+  float acc = 0.f;
+  for (int j = 0; j < p.heads; ++j) {
+    float d = 0.f;
+    for (int c = 0; c < dim; ++c) d = fmaf(qs[j * dim + c], kr[c], d);
+    acc = fmaf(wsh[j], fmaxf(d, 0.f), acc);
+  }
+  out[s] = acc + 0.0f;
+}
+
+// ---------------------------------------------------------------- MFMA tiles
+template <int DT, int D>
+struct Cfg {
+  static constexpr int ES = DT == DT_BF16 ? 2 : 1;          // element size
+  static constexpr int ROWB = D * ES;                        // bytes per key row
+  static constexpr int PITCH = ROWB + 16;                    // LDS row pitch (bank spread)
+  static constexpr int KSTEP = DT == DT_BF16 ? 16 : 64;      // MFMA K per instruction
+  static constexpr int NKS = D / KSTEP;
+  static constexpr int CPR = ROWB / 16;                      // 16-byte chunks per row
+  static constexpr int TILE_CHUNKS = kTileKeys * CPR;
+  static constexpr int NCH = TILE_CHUNKS / 256;              // chunks per thread
+  static constexpr int TILE_BYTES = kTileKeys * PITCH;
+};
+
+template <int DT>
+struct AFrag;
+template <>
+struct AFrag<DT_BF16> { typedef bf16x8 T; };
+template <>
+struct AFrag<DT_FP8> { typedef i32x8 T; };
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma(const typename AFrag<DT>::T& a, const typename AFrag<DT>::T& b,
+                                       f32x16 c) {
+  if constexpr (DT == DT_BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  }
+}
+
+// Load this lane's K-slice of one operand row: for bf16, 8 elements starting at
+// element 16*ks + 8*(lane/32); for fp8, 32 bytes starting at 64*ks + 32*(lane/32).
+// The same slice map is used for q (A) and k (B), so each dot product covers
+// every element of the row exactly once.
+template <int DT>
+__device__ __forceinline__ typename AFrag<DT>::T load_frag(const uint8_t* rowp, int ks, int lane) {
+  if constexpr (DT == DT_BF16) {
+    return *(const bf16x8*)(rowp + (16 * ks + 8 * (lane >> 5)) * 2);
+  } else {
+    const i32x4* p = (const i32x4*)(rowp + 64 * ks + 32 * (lane >> 5));
+    i32x4 lo = p[0], hi = p[1];
+    i32x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+  }
+}
+
+template <int DT, int D, int HT>
+struct RowState {
+  typename AFrag<DT>::T a[HT][Cfg<DT, D>::NKS];
+  float c[HT][16];
+};
+
+// q fragments and per-(row, head) epilogue weights of query row `gi` (flattened
+// batch*n_q index).  Heads >= H are zero rows with zero weight.
+template <int DT, int D, int HT>
+__device__ __forceinline__ void load_row(const IxParams& p, int64_t gi, int lane,
+                                         RowState<DT, D, HT>& rs) {
+  typedef Cfg<DT, D> C;
+  const uint8_t* qb = (const uint8_t*)p.q;
+#pragma unroll
+  for (int h = 0; h < HT; ++h) {
+    const int head = 32 * h + (lane & 31);
+    if (head < p.heads) {
+      const uint8_t* rowp = qb + ((gi * p.heads + head) * (int64_t)D) * C::ES;
+#pragma unroll
+      for (int ks = 0; ks < C::NKS; ++ks) rs.a[h][ks] = load_frag<DT>(rowp, ks, lane);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < C::NKS; ++ks) rs.a[h][ks] = typename AFrag<DT>::T{};
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int hh = 32 * h + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      float cv = 0.f;
+      if (hh < p.heads) {
+        cv = p.w[gi * p.heads + hh];
+        if constexpr (DT == DT_FP8) cv *= p.q_scale[gi * p.heads + hh];
+      }
+      rs.c[h][i] = cv;
+    }
+  }
+}
+
+// Scores of keys [s0, s0+64) for the wave's row; lane l gets key s0 + l.
+// kt: LDS tile (PITCH-byte rows) or, when kt_global, the k row of key s0.
+template <int DT, int D, int HT>
+__device__ __forceinline__ float tile_scores(const RowState<DT, D, HT>& rs, const uint8_t* kt,
+                                             int pitch, int lane) {
+  typedef Cfg<DT, D> C;
+  f32x16 acc[HT][2];
+#pragma unroll
+  for (int h = 0; h < HT; ++h) { acc[h][0] = f32x16{}; acc[h][1] = f32x16{}; }
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      typename AFrag<DT>::T bf = load_frag<DT>(kt + (32 * n + (lane & 31)) * pitch, ks, lane);
+#pragma unroll
+      for (int h = 0; h < HT; ++h) acc[h][n] = mfma<DT>(rs.a[h][ks], bf, acc[h][n]);
+    }
+  }
+  // 32x32 output: lane l holds column (key) l%32 and rows 8*(i/4) + 4*(l/32) + i%4.
+  float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+  for (int h = 0; h < HT; ++h) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      p0 = fmaf(rs.c[h][i], fmaxf(acc[h][0][i], 0.f), p0);
+      p1 = fmaf(rs.c[h][i], fmaxf(acc[h][1][i], 0.f), p1);
+    }
+  }
+  // lanes l and l^32 hold complementary head rows of the same key column:
+  // lanes 0-31 finish keys 0-31 (subtile 0), lanes 32-63 keys 32-63 (subtile 1).
+  const bool lo = lane < 32;
+  const float send = lo ? p1 : p0;
+  const float recv = __shfl_xor(send, 32, 64);
+  return (lo ? p0 : p1) + recv;
+}
+
+// ---------------------------------------------------------------- wave select
+__device__ __forceinline__ void lds_sync() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup"); }
+
+// k-th largest key T among cu[0..n) and how many entries equal to T are kept.
+__device__ void wave_radix_select(const uint32_t* cu, int n, int k, uint32_t* hist, int lane,
+                                  uint32_t& T, uint32_t& req) {
+  uint32_t prefix = 0, mask = 0, rem = (uint32_t)k;
+#pragma unroll 1
+  for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hist[lane * 4 + j] = 0u;
+    lds_sync();
+    for (int j = lane; j < n; j += 64) {
+      uint32_t u = cu[j];
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+    }
+    lds_sync();
+    // lane owns bins 255-4*lane .. 252-4*lane (descending order)
+    uint32_t c0 = hist[255 - 4 * lane], c1 = hist[254 - 4 * lane];
+    uint32_t c2 = hist[253 - 4 * lane], c3 = hist[252 - 4 * lane];
+    uint32_t local = c0 + c1 + c2 + c3, tot;
+    uint32_t ex = wave_excl_scan(local, &tot);
+    bool mine = ex < rem && rem <= ex + local;
+    uint32_t digit = 0, nrem = 0;
+    if (mine) {
+      uint32_t cc = ex;
+      uint32_t cs[4] = {c0, c1, c2, c3};
+      for (int j = 0; j < 4; ++j) {
+        if (cc + cs[j] >= rem) { digit = 255u - 4u * lane - j; nrem = rem - cc; break; }
+        cc += cs[j];
+      }
+    }
+    uint64_t m = ballot(mine);
+    int src = __builtin_ctzll(m);
+    digit = __shfl(digit, src, 64);
+    nrem = __shfl(nrem, src, 64);
+    prefix |= digit << shift;
+    mask |= 0xFFu << shift;
+    rem = nrem;
+    lds_sync();
+  }
+  T = prefix;
+  req = rem;
+}
+
+// Keep the top k of cu/ci[0..n) in position order.  Writes to (du, di) which may
+// alias (cu, ci) (in-place, stable).  Returns the number kept (== k when n >= k).
+__device__ int wave_compact(uint32_t* cu, uint32_t* ci, int n, uint32_t T, uint32_t req, int lane,
+                            uint32_t* du, int32_t* di_global, uint32_t* di_lds, int limit) {
+  int out = 0;
+  uint32_t eqseen = 0;
+  for (int j0 = 0; j0 < n; j0 += 64) {
+    const int j = j0 + lane;
+    const bool in = j < n;
+    const uint32_t u = in ? cu[j] : 0u;
+    const uint32_t id = in ? ci[j] : 0u;
+    const bool tie = in && u == T;
+    const uint64_t tm = ballot(tie);
+    const uint32_t trank = eqseen + lanes_below(tm);
+    const bool keep = in && (u > T || (tie && trank < req));
+    eqseen += (uint32_t)__builtin_popcountll(tm);
+    const uint64_t km = ballot(keep);
+    if (keep) {
+      const int d = out + (int)lanes_below(km);
+      if (di_global) {
+        if (d < limit) di_global[d] = (int32_t)id;
+      } else if (d < limit) {
+        du[d] = u;
+        di_lds[d] = id;
+      }
+    }
+    out += __builtin_popcountll(km);
+  }
+  lds_sync();
+  return out;
+}
+
+// ---------------------------------------------------------------- prefill kernel
+template <int DT, int D, int HT, int MODE>
+__global__ __launch_bounds__(256, 1) void ix_tile_kernel(IxParams p) {
+  typedef Cfg<DT, D> C;
+  __shared__ __attribute__((aligned(16))) uint8_t ktile[2][C::TILE_BYTES];
+  __shared__ uint32_t cand_u[MODE == MODE_TOPK ? kRowsPerBlock : 1][MODE == MODE_TOPK ? kCandCap : 1];
+  __shared__ uint32_t cand_i[MODE == MODE_TOPK ? kRowsPerBlock : 1][MODE == MODE_TOPK ? kCandCap : 1];
+  __shared__ uint32_t hist[MODE == MODE_TOPK ? kRowsPerBlock : 1][256];
+
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t nrb = (p.rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int b = (int)(blockIdx.x % p.batch);
+  const int64_t rb = nrb - 1 - (int64_t)(blockIdx.x / p.batch);   // heaviest rows first
+  const int64_t rloc0 = rb * kRowsPerBlock;                          // within the window
+  const int64_t rloc = rloc0 + wid;
+  const bool vrow = rloc < p.rows;
+  const int64_t i = p.row0 + rloc;                                   // query row
+  const int64_t t = p.q_pos0 + i;
+  const int64_t rlast = (rloc0 + kRowsPerBlock - 1 < p.rows ? rloc0 + kRowsPerBlock - 1 : p.rows - 1);
+  const int64_t t_last = p.q_pos0 + p.row0 + rlast;
+  int64_t nkeys;
+  if (MODE == MODE_SCORES) nkeys = p.n_k;
+  else nkeys = t_last + 1 < p.n_k ? t_last + 1 : p.n_k;
+  const int ntiles = (int)((nkeys + kTileKeys - 1) / kTileKeys);
+  const int64_t gi = (int64_t)b * p.n_q + i;
+
+  RowState<DT, D, HT> rs;
+  if (vrow) load_row<DT, D, HT>(p, gi, lane, rs);
+
+  const uint8_t* kbase = (const uint8_t*)p.k + (int64_t)b * p.k_bs * C::ES;
+  const float* ksc = (DT == DT_FP8) ? p.k_scale + (int64_t)b * p.ks_bs : nullptr;
+
+  i32x4 pre[C::NCH];
+  auto gload = [&](int tile) {
+#pragma unroll
+    for (int j = 0; j < C::NCH; ++j) {
+      const int c = threadIdx.x + 256 * j;
+      const int key = c / C::CPR, part = c % C::CPR;
+      const int64_t s = (int64_t)tile * kTileKeys + key;
+      pre[j] = s < p.n_k ? *(const i32x4*)(kbase + s * C::ROWB + part * 16) : i32x4{};
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < C::NCH; ++j) {
+      const int c = threadIdx.x + 256 * j;
+      const int key = c / C::CPR, part = c % C::CPR;
+      *(i32x4*)(&ktile[buf][key * C::PITCH + part * 16]) = pre[j];
+    }
+  };
+
+  // candidate state (MODE_TOPK)
+  int cnt = 0;
+  bool full = false;
+  uint32_t thr = 0;
+  const int k = p.topk;
+
+  if (ntiles > 0) { gload(0); lstore(0); }
+  for (int it = 0; it < ntiles; ++it) {
+    __syncthreads();
+    if (it + 1 < ntiles) gload(it + 1);
+    const int64_t s0 = (int64_t)it * kTileKeys;
+    if (vrow && (MODE == MODE_SCORES || s0 <= t)) {
+      float sc = tile_scores<DT, D, HT>(rs, &ktile[it & 1][0], C::PITCH, lane);
+      const int64_t s = s0 + lane;
+      if constexpr (DT == DT_FP8) {
+        if (s < p.n_k) sc *= ksc[s];
+      }
+      const bool valid = s <= t && s < p.n_k;
+      if constexpr (MODE == MODE_SCORES) {
+        if (s < p.n_k) {
+          float* out = p.out + ((int64_t)b * p.rows + rloc) * p.n_k;
+          out[s] = valid ? sc + 0.0f : -__builtin_inff();
+        }
+      } else {
+        const uint32_t u = order_key(sc);
+        const bool pred = valid && (!full || u > thr);
+        if (cnt + 64 > kCandCap) {
+          uint32_t T, req;
+          wave_radix_select(cand_u[wid], cnt, k, hist[wid], lane, T, req);
+          cnt = wave_compact(cand_u[wid], cand_i[wid], cnt, T, req, lane, cand_u[wid], nullptr,
+                             cand_i[wid], kCandCap);
+          full = true;
+          thr = T;
+        }
+        const bool pr = pred && (!full || u > thr);
+        const uint64_t m = ballot(pr);
+        if (pr) {
+          const int d = cnt + (int)lanes_below(m);
+          cand_u[wid][d] = u;
+          cand_i[wid][d] = (uint32_t)s;
+        }
+        cnt += __builtin_popcountll(m);
+      }
+    }
+    if (it + 1 < ntiles) lstore((it + 1) & 1);
+  }
+
+  if constexpr (MODE == MODE_TOPK) {
+    if (!vrow) return;
+    lds_sync();
+    int32_t* out = p.idx + gi * (int64_t)k;
+    int nout;
+    if (cnt > k) {
+      uint32_t T, req;
+      wave_radix_select(cand_u[wid], cnt, k, hist[wid], lane, T, req);
+      nout = wave_compact(cand_u[wid], cand_i[wid], cnt, T, req, lane, nullptr, out, nullptr, k);
+      nout = nout < k ? nout : k;
+    } else {
+      for (int j = lane; j < cnt; j += 64) out[j] = (int32_t)cand_i[wid][j];
+      nout = cnt;
+    }
+    for (int j = nout + lane; j < k; j += 64) out[j] = -1;
+  }
+}
+
+// ---------------------------------------------------------------- decode scan
+constexpr int kScanStagesPerWave = 8;  // 64 keys each
+constexpr int kScanSlice = kTileKeys * kScanStagesPerWave * 4;
+
+template <int DT, int D, int HT>
+__global__ __launch_bounds__(256, 2) void ix_scan_kernel(IxParams p) {
+  typedef Cfg<DT, D> C;
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t gi = blockIdx.y;                  // flattened (batch, query row)
+  const int b = (int)(gi / p.n_q);
+  const int64_t i = gi % p.n_q;
+  const int64_t t = p.q_pos0 + i;
+  const int64_t len = t + 1 < p.n_k ? t + 1 : p.n_k;
+  const int64_t slice0 = (int64_t)blockIdx.x * kScanSlice;
+  if (slice0 >= len) return;
+  RowState<DT, D, HT> rs;
+  load_row<DT, D, HT>(p, gi, lane, rs);
+  const uint8_t* kbase = (const uint8_t*)p.k + (int64_t)b * p.k_bs * C::ES;
+  const float* ksc = (DT == DT_FP8) ? p.k_scale + (int64_t)b * p.ks_bs : nullptr;
+  float* out = p.out + gi * (int64_t)p.n_k;
+#pragma unroll 1
+  for (int st = 0; st < kScanStagesPerWave; ++st) {
+    const int64_t s0 = slice0 + (int64_t)(wid + 4 * st) * kTileKeys;
+    if (s0 >= len) break;
+    // B operand straight from HBM; rows past the end read key len-1 (masked).
+    const int64_t srow = s0 + (lane & 31);
+    const int64_t s_a = srow < len ? srow : len - 1;
+    const int64_t s_b = srow + 32 < len ? srow + 32 : len - 1;
+    const uint8_t* base_a = kbase + s_a * C::ROWB;
+    const uint8_t* base_b = kbase + s_b * C::ROWB;
+    f32x16 acc[HT][2];
+#pragma unroll
+    for (int h = 0; h < HT; ++h) { acc[h][0] = f32x16{}; acc[h][1] = f32x16{}; }
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      typename AFrag<DT>::T b0 = load_frag<DT>(base_a, ks, lane);
+      typename AFrag<DT>::T b1 = load_frag<DT>(base_b, ks, lane);
+#pragma unroll
+      for (int h = 0; h < HT; ++h) {
+        acc[h][0] = mfma<DT>(rs.a[h][ks], b0, acc[h][0]);
+        acc[h][1] = mfma<DT>(rs.a[h][ks], b1, acc[h][1]);
+      }
+    }
+    float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+    for (int h = 0; h < HT; ++h) {
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii) {
+        p0 = fmaf(rs.c[h][ii], fmaxf(acc[h][0][ii], 0.f), p0);
+        p1 = fmaf(rs.c[h][ii], fmaxf(acc[h][1][ii], 0.f), p1);
+      }
+    }
+    const bool lo = lane < 32;
+    const float send = lo ? p1 : p0;
+    const float recv = __shfl_xor(send, 32, 64);
+    float sc = (lo ? p0 : p1) + recv;
+    const int64_t s = s0 + lane;
+    if (s < len) {
+      if constexpr (DT == DT_FP8) sc *= ksc[s];
+      out[s] = sc + 0.0f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dispatch
+IxParams make_params(const dsa_indexer_args& a) {
+  IxParams p{};
+  p.q = a.q;
+  p.q_scale = a.q_scale;
+  p.k = a.k;
+  p.k_bs = a.k_batch_stride ? a.k_batch_stride : (int64_t)a.n_k * a.dim;
+  p.k_scale = a.k_scale;
+  p.ks_bs = a.k_scale_batch_stride ? a.k_scale_batch_stride : (int64_t)a.n_k;
+  p.w = a.w;
+  p.batch = a.batch;
+  p.n_q = a.n_q;
+  p.n_k = a.n_k;
+  p.heads = a.heads;
+  p.q_pos0 = a.q_pos0;
+  p.row0 = 0;
+  p.rows = a.n_q;
+  return p;
+}
+
+template <int MODE, int DT, int D>
+hipError_t launch_tile_dt(const IxParams& p, hipStream_t s) {
+  const int64_t nrb = (p.rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  dim3 grid((unsigned)(nrb * p.batch));
+  if (p.heads > 32) {
+    hipLaunchKernelGGL((ix_tile_kernel<DT, D, 2, MODE>), grid, dim3(256), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((ix_tile_kernel<DT, D, 1, MODE>), grid, dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_tile(const dsa_indexer_args& a, const IxParams& p, hipStream_t s) {
+  if (a.dtype == DSA_BF16) {
+    if (a.dim == 128) return launch_tile_dt<MODE, DT_BF16, 128>(p, s);
+    if (a.dim == 64) return launch_tile_dt<MODE, DT_BF16, 64>(p, s);
+    if (a.dim == 32) return launch_tile_dt<MODE, DT_BF16, 32>(p, s);
+  } else if (a.dtype == DSA_FP8_E4M3) {
+    if (a.dim == 128) return launch_tile_dt<MODE, DT_FP8, 128>(p, s);
+    if (a.dim == 64) return launch_tile_dt<MODE, DT_FP8, 64>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int DT, int D>
+hipError_t launch_scan_dt(const IxParams& p, hipStream_t s) {
+  const int64_t len = p.q_pos0 + p.n_q < p.n_k ? p.q_pos0 + p.n_q : p.n_k;
+  dim3 grid((unsigned)((len + kScanSlice - 1) / kScanSlice), (unsigned)((int64_t)p.batch * p.n_q));
+  if (p.heads > 32) {
+    hipLaunchKernelGGL((ix_scan_kernel<DT, D, 2>), grid, dim3(256), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((ix_scan_kernel<DT, D, 1>), grid, dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+namespace dsa_host {
+
+bool indexer_mfma_supported(const dsa_indexer_args& a) {
+  if (a.heads < 1 || a.heads > 64) return false;
+  if (a.dtype == DSA_BF16) return a.dim == 32 || a.dim == 64 || a.dim == 128;
+  if (a.dtype == DSA_FP8_E4M3) return a.dim == 64 || a.dim == 128;
+  return false;
+}
+
+hipError_t indexer_scores_f32(const dsa_indexer_args& a, int64_t row0, int64_t rows, float* out,
+                              int64_t out_row_stride, hipStream_t s) {
+  IxParams p = make_params(a);
+  p.row0 = row0;
+  p.rows = rows;
+  p.out = out;
+  dim3 grid((unsigned)((a.n_k + 255) / 256), (unsigned)rows, (unsigned)a.batch);
+  size_t lds = (size_t)(a.heads * a.dim + a.heads) * sizeof(float);
+  hipLaunchKernelGGL(indexer_f32_kernel, grid, dim3(256), lds, s, p, a.dim, out_row_stride);
+  return hipGetLastError();
+}
+
+hipError_t indexer_scores_mfma(const dsa_indexer_args& a, int64_t row0, int64_t rows, float* out,
+                               hipStream_t s) {
+  IxParams p = make_params(a);
+  p.row0 = row0;
+  p.rows = rows;
+  p.out = out;
+  return launch_tile<MODE_SCORES>(a, p, s);
+}
+
+hipError_t indexer_topk_fused(const dsa_indexer_args& a, int32_t k, int32_t* idx, hipStream_t s) {
+  IxParams p = make_params(a);
+  p.idx = idx;
+  p.topk = k;
+  return launch_tile<MODE_TOPK>(a, p, s);
+}
+
+hipError_t indexer_scan(const dsa_indexer_args& a, float* scores, void* /*sel_ws*/, int32_t /*k*/,
+                        hipStream_t s) {
+  IxParams p = make_params(a);
+  p.out = scores;
+  if (a.dtype == DSA_BF16) {
+    if (a.dim == 128) return launch_scan_dt<DT_BF16, 128>(p, s);
+    if (a.dim == 64) return launch_scan_dt<DT_BF16, 64>(p, s);
+    if (a.dim == 32) return launch_scan_dt<DT_BF16, 32>(p, s);
+  } else if (a.dtype == DSA_FP8_E4M3) {
+    if (a.dim == 128) return launch_scan_dt<DT_FP8, 128>(p, s);
+    if (a.dim == 64) return launch_scan_dt<DT_FP8, 64>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dsa_host

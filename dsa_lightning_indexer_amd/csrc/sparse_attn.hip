@@ -1,0 +1,337 @@
+// Sparse core attention over selected positions ([DSA-NOTES] §3, equation for o_t):
+//     o[h] = sum_{s in T} softmax_s(scale * Q[h] . K[s]) V[s]
+//
+//  * sa_generic_kernel  any shape, fp32 or bf16, one workgroup per (query row,
+//    head): logits in LDS, block max/sum, then P.V with coalesced V reads.
+//  * sa_mla_kernel      bf16 MLA latent layout on MFMA: 16 query heads share one
+//    576-wide latent row per position whose first 512 columns are V.  One
+//    workgroup per (query row, split of the index row); each wave takes 16
+//    selected positions at a time:
+//      S^T[16 keys x 16 heads] = K_sel . Q^T     (16x16x32 bf16 MFMA, K rows
+//                                                 gathered straight from HBM)
+//      online softmax per head (the S^T layout gives each lane one head)
+//      O^T[512 x 16] += V_sel^T . P^T           (16x16x16 bf16 MFMA; V^T comes
+//                                                 from the gathered rows via LDS)
+//    P^T needs no data movement: the S^T accumulator layout (lane = head,
+//    registers = 4 consecutive keys) is exactly the B-operand layout of the
+//    16x16x16 MFMA.  Waves are merged in LDS at the end; with several splits
+//    per row the partial (max, sum, O) go to the workspace and
+//    sa_combine_kernel merges them.
+#include "common.hpp"
+
+namespace {
+
+using namespace dsa;
+
+struct SAParams {
+  int32_t dtype;
+  int32_t batch, n_q, n_k, heads, kv_heads, d_qk, d_v, topk;
+  const void* q;
+  const void* kv;
+  int64_t kv_bs;
+  const void* v;
+  int64_t v_bs;
+  const int32_t* idx;
+  float scale;
+  float* out;
+  int32_t nsplit;
+  float* ws_o;    // [rows, nsplit, heads, d_v]
+  float* ws_ml;   // [rows, nsplit, heads, 2]
+};
+
+__device__ __forceinline__ float ldf(const void* base, int64_t i, bool bf16) {
+  if (bf16) return bf16_bits_to_f32(((const uint16_t*)base)[i]);
+  return ((const float*)base)[i];
+}
+
+__device__ float block_reduce(float v, float* sh, bool is_max) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = is_max ? wave_max(v) : wave_sum(v);
+  if (lane == 0) sh[wid] = v;
+  __syncthreads();
+  float r = sh[0];
+  for (int w = 1; w < nw; ++w) r = is_max ? fmaxf(r, sh[w]) : r + sh[w];
+  __syncthreads();
+  return r;
+}
+
+// ---------------------------------------------------------------- generic path
+__global__ __launch_bounds__(256) void sa_generic_kernel(SAParams p) {
+  extern __shared__ float smem[];
+  float* qs = smem;                   // d_qk
+  float* z = smem + p.d_qk;           // topk
+  __shared__ float red[16];
+  const int h = blockIdx.x % p.heads;
+  const int64_t gi = blockIdx.x / p.heads;      // flattened (b, i)
+  const int b = (int)(gi / p.n_q);
+  const bool bf = p.dtype == DSA_BF16;
+  const int hk = h * p.kv_heads / p.heads;
+  for (int c = threadIdx.x; c < p.d_qk; c += blockDim.x) qs[c] = ldf(p.q, (gi * p.heads + h) * (int64_t)p.d_qk + c, bf);
+  __syncthreads();
+  const int32_t* ir = p.idx + gi * (int64_t)p.topk;
+  float mx = -__builtin_inff();
+  for (int e = threadIdx.x; e < p.topk; e += blockDim.x) {
+    const int32_t s = ir[e];
+    float zz = -__builtin_inff();
+    if (s >= 0 && s < p.n_k) {
+      const int64_t kb = (int64_t)b * p.kv_bs + ((int64_t)s * p.kv_heads + hk) * p.d_qk;
+      float d = 0.f;
+      for (int c = 0; c < p.d_qk; ++c) d = fmaf(qs[c], ldf(p.kv, kb + c, bf), d);
+      zz = d * p.scale;
+    }
+    z[e] = zz;
+    mx = fmaxf(mx, zz);
+  }
+  mx = block_reduce(mx, red, true);
+  float sum = 0.f;
+  for (int e = threadIdx.x; e < p.topk; e += blockDim.x) {
+    const float pe = (mx == -__builtin_inff() || z[e] == -__builtin_inff()) ? 0.f : __expf(z[e] - mx);
+    z[e] = pe;
+    sum += pe;
+  }
+  sum = block_reduce(sum, red, false);
+  __syncthreads();
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
+  float* out = p.out + (gi * p.heads + h) * (int64_t)p.d_v;
+  const void* vb = p.v ? p.v : p.kv;
+  const int64_t vrow = p.v ? (int64_t)p.kv_heads * p.d_v : (int64_t)p.kv_heads * p.d_qk;
+  const int64_t vhead = p.v ? p.d_v : p.d_qk;
+  const int64_t vbs = p.v ? p.v_bs : p.kv_bs;
+  for (int c = threadIdx.x; c < p.d_v; c += blockDim.x) {
+    float acc = 0.f;
+    for (int e = 0; e < p.topk; ++e) {
+      const float pe = z[e];
+      if (pe != 0.f) {
+        const int32_t s = ir[e];
+        acc = fmaf(pe, ldf(vb, (int64_t)b * vbs + (int64_t)s * vrow + hk * vhead + c, bf), acc);
+      }
+    }
+    out[c] = acc * inv;
+  }
+}
+
+// ---------------------------------------------------------------- MLA MFMA path
+constexpr int kH = 16;       // query heads per latent row
+constexpr int kTile = 16;    // selected positions per wave step
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(256, 1) void sa_mla_kernel(SAParams p) {
+  constexpr int NKS = DQK / 32;        // 16x16x32 K steps for Q.K
+  constexpr int NVS = DV / 32;         // of those, the ones that carry V columns
+  constexpr int NDT = DV / 16;         // output tiles of 16 V columns
+  __shared__ __attribute__((aligned(16))) __bf16 vt[4][DV][kTile];   // V^T per wave
+  __shared__ float obuf[kH][DV];
+  __shared__ float sm[4][kH], sl[4][kH];
+
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, col = lane & 15;
+  const int split = (int)(blockIdx.x % p.nsplit);
+  const int64_t gi = blockIdx.x / p.nsplit;          // flattened (batch, query row)
+  const int b = (int)(gi / p.n_q);
+  const int per = (p.topk + p.nsplit - 1) / p.nsplit;
+  const int e0 = split * per;
+  const int e1 = e0 + per < p.topk ? e0 + per : p.topk;
+
+  // Q^T as the B operand: lane holds head `col`, dims 32*ks + 8*g .. +8.
+  bf16x8 qf[NKS];
+  const __bf16* qrow = (const __bf16*)p.q + (gi * kH + col) * (int64_t)DQK;
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8*)(qrow + 32 * ks + 8 * g);
+
+  f32x4 o[NDT];
+#pragma unroll
+  for (int d = 0; d < NDT; ++d) o[d] = f32x4{};
+  float m_run = -__builtin_inff(), l_run = 0.f;
+
+  const __bf16* kvb = (const __bf16*)p.kv + (int64_t)b * p.kv_bs;
+  const int32_t* ir = p.idx + gi * (int64_t)p.topk;
+
+  for (int tb = e0 + kTile * wid; tb < e1; tb += 4 * kTile) {
+    const int e = tb + col;
+    int32_t s = e < e1 ? ir[e] : -1;
+    const bool valid = s >= 0 && s < p.n_k;
+    const uint64_t vm = ballot(valid);
+    const __bf16* rowp = kvb + (int64_t)(valid ? s : 0) * DQK;
+    f32x4 acc = f32x4{};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      bf16x8 a = valid ? *(const bf16x8*)(rowp + 32 * ks + 8 * g) : bf16x8{};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], acc, 0, 0, 0);
+      if (ks < NVS) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vt[wid][32 * ks + 8 * g + j][col] = a[j];
+      }
+    }
+    // acc[i]: head `col`, key 4*g + i of this tile.
+    float z[4];
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool kv_ok = (vm >> (4 * g + i)) & 1ull;
+      z[i] = kv_ok ? acc[i] * p.scale : -__builtin_inff();
+      mx = fmaxf(mx, z[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    bf16x4 pb;
+    float alpha = 1.f;
+    if (m_new == -__builtin_inff()) {
+      pb = bf16x4{};
+    } else {
+      alpha = (m_run == -__builtin_inff()) ? 0.f : __expf(m_run - m_new);
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pe = z[i] == -__builtin_inff() ? 0.f : __expf(z[i] - m_new);
+        const __bf16 pbh = (__bf16)pe;
+        pb[i] = pbh;
+        ps += (float)pbh;       // normalise with the same rounded weights P.V uses
+      }
+      l_run = l_run * alpha + ps;
+      m_run = m_new;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      o[dt] *= alpha;
+      const bf16x4 va = *(const bf16x4*)&vt[wid][16 * dt + col][4 * g];
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[dt], 0, 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  }
+  // Merge the four waves.
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (g == 0) { sm[wid][col] = m_run; sl[wid][col] = l_run; }
+  __syncthreads();
+  float M = -__builtin_inff();
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][col]);
+  float L = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float mw = sm[w][col];
+    L += (mw == -__builtin_inff()) ? 0.f : sl[w][col] * __expf(mw - M);
+  }
+  const float myscale = (m_run == -__builtin_inff()) ? 0.f : __expf(m_run - M);
+  for (int w = 0; w < 4; ++w) {
+    if (wid == w) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = 16 * dt + 4 * g + i;
+          const float v = o[dt][i] * myscale;
+          obuf[col][d] = (w == 0) ? v : obuf[col][d] + v;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (p.nsplit == 1) {
+    // every lane holding head `col` computed the same L; publish it once
+    if (wid == 0 && g == 0) sl[0][col] = L;
+    __syncthreads();
+    float* out = p.out + gi * (int64_t)kH * DV;
+    for (int x = threadIdx.x; x < kH * DV; x += 256) {
+      const int h = x / DV;
+      const float Lh = sl[0][h];
+      out[x] = Lh > 0.f ? obuf[h][x % DV] / Lh : 0.f;
+    }
+  } else {
+    float* wo = p.ws_o + (gi * p.nsplit + split) * (int64_t)kH * DV;
+    for (int x = threadIdx.x; x < kH * DV; x += 256) wo[x] = obuf[x / DV][x % DV];
+    if (wid == 0 && g == 0) {
+      float* ml = p.ws_ml + ((gi * p.nsplit + split) * kH + col) * 2;
+      ml[0] = M;
+      ml[1] = L;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void sa_combine_kernel(SAParams p) {
+  const int h = blockIdx.x % p.heads;
+  const int64_t gi = blockIdx.x / p.heads;
+  float M = -__builtin_inff();
+  for (int sp = 0; sp < p.nsplit; ++sp) M = fmaxf(M, p.ws_ml[((gi * p.nsplit + sp) * p.heads + h) * 2]);
+  float L = 0.f;
+  for (int sp = 0; sp < p.nsplit; ++sp) {
+    const float* ml = p.ws_ml + ((gi * p.nsplit + sp) * p.heads + h) * 2;
+    L += (ml[0] == -__builtin_inff()) ? 0.f : ml[1] * __expf(ml[0] - M);
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float* out = p.out + (gi * p.heads + h) * (int64_t)p.d_v;
+  for (int c = threadIdx.x; c < p.d_v; c += blockDim.x) {
+    float acc = 0.f;
+    for (int sp = 0; sp < p.nsplit; ++sp) {
+      const float m = p.ws_ml[((gi * p.nsplit + sp) * p.heads + h) * 2];
+      if (m == -__builtin_inff()) continue;
+      acc += p.ws_o[((gi * p.nsplit + sp) * p.heads + h) * (int64_t)p.d_v + c] * __expf(m - M);
+    }
+    out[c] = acc * inv;
+  }
+}
+
+bool mla_ok(const dsa_sparse_attn_args& a) {
+  return a.dtype == DSA_BF16 && a.heads == kH && a.kv_heads == 1 && a.d_qk == 576 &&
+         a.d_v == 512 && a.v == nullptr;
+}
+
+int pick_nsplit(const dsa_sparse_attn_args& a) {
+  const int64_t rows = (int64_t)a.batch * a.n_q;
+  int64_t ns = (512 + rows - 1) / rows;
+  int64_t maxs = a.topk / 64;
+  if (maxs < 1) maxs = 1;
+  if (ns > maxs) ns = maxs;
+  if (ns < 1) ns = 1;
+  return (int)ns;
+}
+
+SAParams make(const dsa_sparse_attn_args& a) {
+  SAParams p{};
+  p.dtype = a.dtype;
+  p.batch = a.batch; p.n_q = a.n_q; p.n_k = a.n_k; p.heads = a.heads; p.kv_heads = a.kv_heads;
+  p.d_qk = a.d_qk; p.d_v = a.d_v; p.topk = a.topk;
+  p.q = a.q; p.kv = a.kv; p.v = a.v; p.idx = a.idx; p.scale = a.scale; p.out = a.out;
+  p.kv_bs = a.kv_batch_stride ? a.kv_batch_stride : (int64_t)a.n_k * a.kv_heads * a.d_qk;
+  p.v_bs = a.v_batch_stride ? a.v_batch_stride : (int64_t)a.n_k * a.kv_heads * a.d_v;
+  p.nsplit = 1;
+  return p;
+}
+
+}  // namespace
+
+namespace dsa_host {
+
+size_t sparse_attn_ws_bytes(const dsa_sparse_attn_args& a) {
+  if (!mla_ok(a)) return 0;
+  const int ns = pick_nsplit(a);
+  if (ns == 1) return 0;
+  const int64_t rows = (int64_t)a.batch * a.n_q;
+  return (size_t)rows * ns * a.heads * ((size_t)a.d_v + 2) * sizeof(float);
+}
+
+hipError_t sparse_attn_launch(const dsa_sparse_attn_args& a, void* ws, hipStream_t s) {
+  SAParams p = make(a);
+  if (mla_ok(a)) {
+    p.nsplit = pick_nsplit(a);
+    const int64_t rows = (int64_t)a.batch * a.n_q;
+    if (p.nsplit > 1) {
+      p.ws_o = (float*)ws;
+      p.ws_ml = p.ws_o + rows * p.nsplit * a.heads * (int64_t)a.d_v;
+    }
+    dim3 grid((unsigned)(rows * p.nsplit));
+    hipLaunchKernelGGL((sa_mla_kernel<576, 512>), grid, dim3(256), 0, s, p);
+    if (p.nsplit > 1) {
+      hipLaunchKernelGGL(sa_combine_kernel, dim3((unsigned)(rows * a.heads)), dim3(256), 0, s, p);
+    }
+    return hipGetLastError();
+  }
+  const size_t lds = ((size_t)a.d_qk + a.topk) * sizeof(float);
+  dim3 grid((unsigned)((int64_t)a.batch * a.n_q * a.heads));
+  hipLaunchKernelGGL(sa_generic_kernel, grid, dim3(256), lds, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace dsa_host

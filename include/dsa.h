@@ -1,0 +1,196 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) DeepSeek-Sparse-Attention step with
+ * IndexCache cross-layer index reuse.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [DSA-NOTES]  "IndexCache：跨层复用稀疏索引，以及它为什么能被训练"
+ *                (reading notes on IndexCache, notes.kuangjux.top)
+ *   [IC-SUMMARY] "IndexCache: Accelerating Sparse Attention via Cross-Layer
+ *                Index Reuse" (section-by-section summary, papercache.org)
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is a DEVICE pointer unless marked "host".  The
+ *     caller owns every buffer, including the workspace; the library
+ *     allocates no device memory and keeps no state between calls.
+ *   - Layouts are row-major and dense unless a batch stride is given.
+ *     Strides are in elements of the tensor's own type.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream); no
+ *     call synchronises the host with the device.
+ *   - Arguments are validated on the host before anything is enqueued; on a
+ *     non-OK status nothing was enqueued (except DSA_ERR_HIP, which reports
+ *     a launch failure of already-enqueued work).  dsa_last_error() gives a
+ *     thread-local description of the last failure.
+ *   - Query row i of batch b sits at absolute position t = q_pos0 + i.  Its
+ *     indexer candidates are the positions s = 0..min(t, n_k-1) (causal,
+ *     inclusive of s = t).
+ *   - Index tensors hold, per query row, the selected positions in ascending
+ *     order followed by -1 padding.  Rows with fewer than k candidates select
+ *     all of them.  Ties in score go to the lower position; -0.0 equals +0.0.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+#define DSA_MAX_TOPK 2048
+#define DSA_MAX_INDEXER_HEADS 64
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID = 1,      /* a required pointer is NULL, a size is out of range, bad pattern */
+  DSA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (dtype/shape combination) */
+  DSA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than the *_workspace_size() result */
+  DSA_ERR_HIP = 4           /* a HIP launch or runtime call failed */
+} dsa_status;
+
+typedef enum {
+  DSA_F32 = 0,
+  DSA_BF16 = 1,
+  DSA_FP8_E4M3 = 2          /* OCP fp8 e4m3fn (max 448, no infinities) */
+} dsa_dtype;
+
+/*
+ * Inputs of one F layer's lightning indexer ([DSA-NOTES] §2.1, score equation;
+ * [IC-SUMMARY] §2.1):
+ *     I[t, s] = sum_{j < heads} w[t, j] * ReLU(q[t, j, :] . k[s, :])
+ * The key has no head index: one key per token serves every head.
+ *
+ *   q       [batch, n_q, heads, dim]   dtype
+ *   q_scale [batch, n_q, heads] fp32   FP8 only (NULL otherwise): q = q_scale * code
+ *   k       [batch, n_k, dim] dtype, batch stride k_batch_stride (0 = n_k*dim)
+ *   k_scale [batch, n_k] fp32, batch stride k_scale_batch_stride (0 = n_k); FP8 only
+ *   w       [batch, n_q, heads] fp32   dynamic per-token head weights (any sign)
+ * Limits: 1 <= heads <= 64; dim in {32, 64, 128} (F32 accepts 1..256).
+ */
+typedef struct dsa_indexer_args {
+  int32_t dtype;
+  int32_t batch, n_q, n_k, heads, dim;
+  int64_t q_pos0;
+  const void* q;
+  const float* q_scale;
+  const void* k;
+  int64_t k_batch_stride;
+  const float* k_scale;
+  int64_t k_scale_batch_stride;
+  const float* w;
+} dsa_indexer_args;
+
+/*
+ * Inputs of one layer's sparse core attention ([DSA-NOTES] §3, equation for
+ * o_t): for query row (b, i) and head h,
+ *     o = sum_{s in T} softmax_{s in T}(scale * Q[b,i,h,:] . K[b,s,g,:]) V[b,s,g,:]
+ * with T the row's index set and g = h * kv_heads / heads.
+ *
+ *   q   [batch, n_q, heads, d_qk]      dtype (F32 or BF16)
+ *   kv  [batch, n_k, kv_heads, d_qk]   dtype, batch stride kv_batch_stride (0 = dense)
+ *   v   NULL: V is the first d_v columns of each kv row (MLA latent layout);
+ *       else [batch, n_k, kv_heads, d_v], batch stride v_batch_stride (0 = dense)
+ *   idx [batch, n_q, topk] int32; entries outside [0, n_k) (e.g. -1) select
+ *       nothing; a row selecting nothing yields zeros
+ *   out [batch, n_q, heads, d_v] fp32
+ * Limits: d_qk, d_v <= 1024; heads % kv_heads == 0; 1 <= topk <= 2048.
+ */
+typedef struct dsa_sparse_attn_args {
+  int32_t dtype;
+  int32_t batch, n_q, n_k, heads, kv_heads, d_qk, d_v, topk;
+  const void* q;
+  const void* kv;
+  int64_t kv_batch_stride;
+  const void* v;
+  int64_t v_batch_stride;
+  const int32_t* idx;
+  float scale;
+  float* out;
+} dsa_sparse_attn_args;
+
+/* Library version of this header (DSA_ABI_VERSION). */
+int32_t dsa_abi_version(void);
+/* Static text for a status code. */
+const char* dsa_status_string(int32_t status);
+/* Thread-local text of the last failure of a call made on this thread ("" if none). */
+const char* dsa_last_error(void);
+
+/*
+ * INDEXER, materialised ([DSA-NOTES] §2.1).  Writes the scores of query rows
+ * [row0, row0 + rows) of every batch into scores[b][r][s] (fp32, dense
+ * [batch, rows, n_k]); positions s > t are written as -inf.  For inspection and
+ * for callers that want the scores; the Top-k path below never materialises them.
+ */
+dsa_status dsa_indexer_scores(const dsa_indexer_args* args, int64_t row0, int64_t rows,
+                              float* scores, hipStream_t stream);
+
+/*
+ * Top-k ([IC-SUMMARY] notation: T_t = Top-k(I_t); Algorithm (b) steps 3-4).
+ *   scores == NULL: score and select in one pass (INDEXER + Top-k).  bf16/fp8
+ *     prefill never writes the score matrix; decode-shaped calls (few query
+ *     rows, long n_k) and F32 inputs stage fp32 scores in the workspace.
+ *   scores != NULL: select from caller scores laid out [batch, n_q, n_k]
+ *     (the dsa_indexer_scores() layout with row0 = 0, rows = n_q); only
+ *     positions s <= t are candidates.  args->q/k/w are then not read.
+ *   k: 1..2048.  idx: [batch, n_q, k] int32 output.
+ *   ws/ws_bytes: workspace of at least dsa_topk_workspace_size() bytes
+ *     (may be NULL when that size is 0).
+ */
+size_t dsa_topk_workspace_size(const dsa_indexer_args* args, const float* scores, int32_t k);
+dsa_status dsa_topk(const dsa_indexer_args* args, const float* scores, int32_t k,
+                    int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* SPARSEATTN ([IC-SUMMARY] Algorithm (b) step 9; [DSA-NOTES] §3). */
+size_t dsa_sparse_attn_workspace_size(const dsa_sparse_attn_args* args);
+dsa_status dsa_sparse_attn(const dsa_sparse_attn_args* args, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/*
+ * One layer of the IndexCache loop.
+ *   ix      F layers: the layer's indexer inputs.  S layers: never read (may be
+ *           all zero / NULL pointers) -- an S layer has no indexer and no
+ *           indexer K cache ([DSA-NOTES] §11.1-11.2).
+ *   sa      the layer's own attention inputs; sa.idx is ignored and replaced
+ *           by the cached index tensor.
+ *   idx_out F layers: [batch, n_q, k] int32 output (becomes the cached index
+ *           tensor).  S layers: never read or written.
+ */
+typedef struct dsa_layer {
+  dsa_indexer_args ix;
+  dsa_sparse_attn_args sa;
+  int32_t* idx_out;
+} dsa_layer;
+
+/*
+ * IndexCache inference loop ([IC-SUMMARY] Algorithm (b) and §3 core
+ * mechanism; [DSA-NOTES] §2.2 FSSS FSSS trace).  pattern (host) is n_layers
+ * characters of 'F'/'S' with pattern[0] == 'F'.  For l = 1..N: an F layer runs
+ * INDEXER + Top-k into its idx_out, which becomes the cached index tensor
+ * (overwriting the previous one); an S layer reuses the cached tensor with no
+ * launch and no copy.  Every layer then runs its own sparse attention on that
+ * tensor.  src_layer (host, optional) receives f(l), the 0-based layer whose
+ * index tensor layer l used.  layers[] is a host array.
+ */
+size_t indexcache_forward_workspace_size(const char* pattern, int32_t n_layers,
+                                         const dsa_layer* layers, int32_t k);
+dsa_status indexcache_forward(const char* pattern, int32_t n_layers, const dsa_layer* layers,
+                              int32_t k, int32_t* src_layer, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/*
+ * Cross-layer overlap ([DSA-NOTES] §3.1; [IC-SUMMARY] Appendix A):
+ * |T_a[r] ∩ T_b[r]| for rows r = 0..rows-1 of two index tensors with k columns
+ * (each row ascending with -1 padding, as produced above).  row_counts
+ * (device int32 [rows], optional) receives each row's count; *total (device
+ * uint64, optional) is incremented by the sum.  overlap = sum / (rows * k).
+ */
+dsa_status dsa_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t rows,
+                             int32_t k, int32_t* row_counts, unsigned long long* total,
+                             hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H_ */

@@ -1,0 +1,168 @@
+"""C-ABI tests that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before anything is enqueued.
+
+Every call here fails validation (or only sizes a workspace), so no kernel is
+ever launched with the fake pointers used below."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+L = pytest.importorskip("dsa_lightning_indexer_amd._lib")
+
+FAKE = 0x7F0000000000   # 256-byte aligned non-NULL value; never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_and_exports_agree():
+    decl = declared_functions()
+    assert set(decl) == set(L.EXPORTS), decl
+    for name in decl:
+        assert hasattr(L.LIB, name), name
+
+
+def test_version_and_status_strings():
+    assert L.abi_version() == 1
+    assert L.dsa_status_string(0) == b"ok"
+    assert b"workspace" in L.dsa_status_string(3)
+
+
+def ix(**kw):
+    a = L.IndexerArgs()
+    a.dtype, a.batch, a.n_q, a.n_k, a.heads, a.dim = L.DSA_BF16, 1, 64, 64, 64, 128
+    a.q = a.k = a.w = FAKE
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def topk_status(a, k=16, idx=FAKE, scores=None, ws=None, ws_bytes=0):
+    return L.dsa_topk(ctypes.byref(a), scores, k, idx, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,k,expect", [
+    (dict(), 0, 1), (dict(), 2049, 1),
+    (dict(dtype=7), 16, 1), (dict(batch=0), 16, 1), (dict(n_k=0), 16, 1), (dict(q_pos0=-1), 16, 1),
+    (dict(heads=65), 16, 2), (dict(heads=0), 16, 2), (dict(dim=96), 16, 2),
+    (dict(dtype=L.DSA_FP8_E4M3, dim=32), 16, 2),
+    (dict(q=None), 16, 1), (dict(w=None), 16, 1),
+    (dict(dtype=L.DSA_FP8_E4M3), 16, 1),                   # fp8 without scales
+    (dict(q=FAKE + 4), 16, 1),                            # misaligned
+    (dict(k_batch_stride=5), 16, 1),
+    (dict(dtype=L.DSA_F32, dim=300), 16, 2),
+])
+def test_topk_rejects(kw, k, expect):
+    assert topk_status(ix(**kw), k=k) == expect
+    assert L.dsa_last_error() != b""
+
+
+def test_topk_null_idx():
+    assert topk_status(ix(), idx=None) == 1
+
+
+def test_workspace_sizes_and_errors():
+    a = ix(batch=8, n_q=1, n_k=204800, q_pos0=204799, dtype=L.DSA_FP8_E4M3, q_scale=FAKE, k_scale=FAKE)
+    need = L.dsa_topk_workspace_size(ctypes.byref(a), None, 2048)
+    assert need >= 8 * 204800 * 4
+    assert topk_status(a, k=2048, ws=None, ws_bytes=0) == 3
+    assert topk_status(a, k=2048, ws=FAKE, ws_bytes=need - 1) == 3
+    # prefill-shaped bf16 fused path needs no workspace
+    b = ix(n_q=16384, n_k=16384)
+    assert L.dsa_topk_workspace_size(ctypes.byref(b), None, 2048) == 0
+    # materialised-scores path needs the select state
+    assert L.dsa_topk_workspace_size(ctypes.byref(b), FAKE, 2048) > 0
+    assert topk_status(b, k=2048, scores=FAKE) == 3
+
+
+def test_indexer_scores_rejects_bad_window():
+    a = ix()
+    assert L.dsa_indexer_scores(ctypes.byref(a), 60, 10, FAKE, None) == 1
+    assert L.dsa_indexer_scores(ctypes.byref(a), -1, 10, FAKE, None) == 1
+    assert L.dsa_indexer_scores(ctypes.byref(a), 0, 0, FAKE, None) == 1
+    assert L.dsa_indexer_scores(ctypes.byref(a), 0, 4, None, None) == 1
+
+
+def sa(**kw):
+    a = L.SparseAttnArgs()
+    a.dtype, a.batch, a.n_q, a.n_k, a.heads, a.kv_heads = L.DSA_BF16, 1, 4, 100, 16, 1
+    a.d_qk, a.d_v, a.topk, a.scale = 576, 512, 2048, 1 / 24
+    a.q = a.kv = a.idx = a.out = FAKE
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dtype=L.DSA_FP8_E4M3), 2), (dict(heads=15, kv_heads=2), 1), (dict(d_v=600), 1),
+    (dict(d_qk=2000), 2), (dict(topk=0), 1), (dict(topk=4096), 1), (dict(idx=None), 1),
+    (dict(out=None), 1), (dict(scale=float("nan")), 1), (dict(kv_batch_stride=10), 1),
+])
+def test_sparse_attn_rejects(kw, expect):
+    assert L.dsa_sparse_attn(ctypes.byref(sa(**kw)), None, 0, None) == expect
+
+
+def test_sparse_attn_decode_needs_workspace():
+    a = sa(batch=8, n_q=1, n_k=204800)
+    need = L.dsa_sparse_attn_workspace_size(ctypes.byref(a))
+    assert need > 0
+    assert L.dsa_sparse_attn(ctypes.byref(a), None, 0, None) == 3
+
+
+def layers(pattern, null_s=True):
+    arr = (L.Layer * len(pattern))()
+    for i, c in enumerate(pattern):
+        if c == "F" or not null_s:
+            arr[i].ix = ix(n_q=4, n_k=4)
+            arr[i].idx_out = FAKE
+        arr[i].sa = sa(n_q=4, n_k=4, topk=16)
+    return arr
+
+
+def fwd_status(pattern, arr, n=None, k=16):
+    n = len(pattern) if n is None else n
+    return L.indexcache_forward_c(pattern.encode(), n, arr, k, None, None, 0, None)
+
+
+def test_forward_pattern_validation():
+    assert fwd_status("SFFF", layers("FFFF")) == 1            # first layer must be F
+    assert fwd_status("FXSS", layers("FFFF")) == 1
+    assert fwd_status("FSS", layers("FSS"), n=4) == 1         # length mismatch
+    assert fwd_status("FSS", layers("FSS"), k=0) == 1
+    assert L.indexcache_forward_c(None, 3, layers("FSS"), 16, None, None, 0, None) == 1
+    assert L.indexcache_forward_c(b"FSS", 3, None, 16, None, None, 0, None) == 1
+
+
+def test_forward_s_layers_need_no_indexer_inputs():
+    """An S layer's indexer arguments are never read: validation (and workspace
+    sizing) succeeds with every S-layer indexer pointer NULL."""
+    arr = layers("FSSSFSSS", null_s=True)
+    assert L.indexcache_forward_workspace_size(b"FSSSFSSS", 8, arr, 16) == 0
+    # the same NULL indexer on an F layer is rejected
+    arr[0].ix = L.IndexerArgs()
+    assert fwd_status("FSSSFSSS", arr) == 1
+
+
+def test_forward_attention_shape_must_match_cached_tensor():
+    arr = layers("FS")
+    arr[1].sa.n_q = 5
+    assert fwd_status("FS", arr) == 1
+    arr = layers("FS")
+    arr[1].sa.topk = 8
+    assert fwd_status("FS", arr) == 1
+
+
+def test_overlap_rejects():
+    assert L.dsa_index_overlap(FAKE, FAKE, 4, 0, FAKE, None, None) == 1
+    assert L.dsa_index_overlap(None, FAKE, 4, 16, FAKE, None, None) == 1
+    assert L.dsa_index_overlap(FAKE, FAKE, 4, 16, None, None, None) == 1
+    assert L.dsa_index_overlap(FAKE, FAKE, -1, 16, FAKE, None, None) == 1

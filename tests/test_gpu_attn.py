@@ -1,0 +1,109 @@
+"""GPU parity of sparse attention and the overlap measure against the oracle.
+Sparse attention: per (row, head) max_c|o_gpu - o_ref| <= 2e-3 * max_c|o_ref|,
+with the index tensor drawn by the seeded generator (never produced by the GPU)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import inputs as syn
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    import dsa_lightning_indexer_amd as m
+    return m
+
+
+def run_sa(dsa, sa, idx):
+    out = dsa.sparse_attn(sa.q, sa.kv, idx, sa.scale, d_v=sa.d_v, v=sa.v)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check_sa(dsa, sa, idx, rows=None):
+    got = run_sa(dsa, sa, idx)
+    B, n_q = sa.q.shape[:2]
+    worst = 0.0
+    for b in range(B):
+        Q, K, V = H.sa_f64(sa, b)
+        rr = np.arange(n_q) if rows is None else rows
+        ref = oracle.sparse_attn(Q, K, V, idx[b].cpu().numpy(), sa.scale, rows=rr)
+        worst = max(worst, H.attn_close(got[b, rr], ref))
+    assert worst <= H.ATTN_RTOL, worst
+    return got
+
+
+def test_c1_fp32_mha(dsa, dev):
+    c = syn.CONFIGS[1]
+    L = c["L"]
+    sa = syn.sa_inputs(n_q=L, n_k=L, heads=4, kv_heads=4, d_qk=64, d_v=64, latent=False, dtype=syn.F32,
+                       seed=c["seed"], device=dev)
+    idx = syn.random_sorted_indices(n_q=L, topk=c["topk"], seed=12, device=dev)
+    check_sa(dsa, sa, idx)
+
+
+def test_mla_prefill_short_and_full_rows(dsa, dev):
+    """16 heads over the 576-wide latent (V = first 512 columns); rows t < 2047
+    carry -1 padding, later rows a full 2048 selection."""
+    n = 2600
+    sa = syn.sa_inputs(n_q=n, n_k=n, seed=3, device=dev)
+    idx = syn.random_sorted_indices(n_q=n, topk=2048, seed=4, device=dev)
+    rows = np.array(sorted(set([0, 1, 2, 15, 16, 17, 500, 2046, 2047, 2048, 2300, n - 1])))
+    check_sa(dsa, sa, idx, rows)
+
+
+def test_mla_decode_split(dsa, dev):
+    """Decode shape (1 query per sequence): the index row is split across
+    workgroups and merged by the combine kernel."""
+    B, S = 3, 9000
+    sa = syn.sa_inputs(B=B, n_q=1, n_k=S, seed=5, device=dev)
+    idx = syn.random_sorted_indices(B=B, n_q=1, topk=2048, q_pos0=S - 1, seed=6, device=dev)
+    check_sa(dsa, sa, idx)
+
+
+def test_mla_invalid_entries_and_empty_rows(dsa, dev):
+    n = 300
+    sa = syn.sa_inputs(n_q=n, n_k=n, seed=7, device=dev)
+    idx = syn.random_sorted_indices(n_q=n, topk=2048, seed=8, device=dev)
+    idx[0, 10] = -1                      # an empty row -> zeros
+    idx[0, 11, :] = n + 5                # out of range -> selects nothing
+    idx[0, 12, 5] = 10 ** 9              # one bad entry among valid ones
+    got = check_sa(dsa, sa, idx, np.arange(0, 40))
+    assert (got[0, 10] == 0).all() and (got[0, 11] == 0).all()
+
+
+@pytest.mark.parametrize("latent,kv_heads,dtype", [(False, 2, syn.BF16), (True, 4, syn.BF16), (False, 1, syn.F32)])
+def test_generic_paths(dsa, dev, latent, kv_heads, dtype):
+    n = 200
+    sa = syn.sa_inputs(n_q=n, n_k=n, heads=8, kv_heads=kv_heads, d_qk=96, d_v=80 if not latent else 64,
+                       latent=latent, dtype=dtype, seed=9, device=dev)
+    idx = syn.random_sorted_indices(n_q=n, topk=100, seed=10, device=dev)
+    check_sa(dsa, sa, idx)
+
+
+def test_sa_determinism(dsa, dev):
+    sa = syn.sa_inputs(B=2, n_q=1, n_k=5000, seed=11, device=dev)
+    idx = syn.random_sorted_indices(B=2, n_q=1, topk=2048, q_pos0=4999, seed=12, device=dev)
+    a = run_sa(dsa, sa, idx)
+    b = run_sa(dsa, sa, idx)
+    assert np.array_equal(a, b)
+
+
+def test_overlap_counts(dsa, dev):
+    k = 256
+    a = syn.random_sorted_indices(n_q=700, topk=k, seed=1, device=dev)[0]
+    b = syn.random_sorted_indices(n_q=700, topk=k, seed=2, device=dev)[0]
+    b[300:400] = a[300:400]
+    counts = torch.zeros(700, dtype=torch.int32, device=dev)
+    total = dsa.index_overlap(a, b, k, row_counts=counts)
+    an, bn = a.cpu().numpy(), b.cpu().numpy()
+    ref = [len(set(an[r][an[r] >= 0]) & set(bn[r][bn[r] >= 0])) for r in range(700)]
+    assert counts.cpu().numpy().tolist() == ref
+    assert int(total.item()) == sum(ref)
+    rows = np.arange(k - 1, 700)
+    ov = sum(ref[r] for r in rows) / (len(rows) * k)
+    assert ov == pytest.approx(oracle.overlap(an, bn, k, rows))

@@ -1,0 +1,195 @@
+"""GPU parity of the indexer and Top-k against the CPU oracle.
+
+Integer-valued inputs: indices bit-exact, scores exactly equal.  Float inputs:
+scores within 1e-3 * A and the index-set tie-window rule (see helpers)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import inputs as syn
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    import dsa_lightning_indexer_amd as m
+    return m
+
+
+def sample_rows(n_q, k, seed, n_random=24):
+    """rows near 0, around k-1, a random sample and the last rows."""
+    r = np.random.default_rng(seed)
+    rows = set(range(min(8, n_q)))
+    rows |= {x for x in range(k - 3, k + 3) if 0 <= x < n_q}
+    rows |= set(r.integers(0, n_q, n_random).tolist())
+    rows |= set(range(max(0, n_q - 4), n_q))
+    return np.array(sorted(rows))
+
+
+def oracle_rows(ixi, b, rows, topk):
+    q, k, w = H.indexer_f64(ixi, b)
+    idx, I, A = oracle.indexer_topk(q, k, w, topk, q_pos0=ixi.q_pos0, rows=rows)
+    return idx, I, A
+
+
+def run_topk(dsa, ixi, topk):
+    out = dsa.topk(ixi.q, ixi.k, ixi.w, topk, q_scale=ixi.q_scale, k_scale=ixi.k_scale, q_pos0=ixi.q_pos0)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_exact(dsa, ixi, topk, rows=None, seed=0):
+    B, n_q = ixi.q.shape[:2]
+    got = run_topk(dsa, ixi, topk).cpu().numpy()
+    for b in range(B):
+        rr = np.arange(n_q) if rows is None else rows
+        ref, _, _ = oracle_rows(ixi, b, rr, topk)
+        mism = np.flatnonzero((got[b, rr] != ref).any(axis=1))
+        assert mism.size == 0, f"batch {b}: {mism.size} rows differ, first row {rr[mism[0]]}"
+    return got
+
+
+def check_float(dsa, ixi, topk, rows):
+    B = ixi.q.shape[0]
+    got = run_topk(dsa, ixi, topk).cpu().numpy()
+    for b in range(B):
+        ref, I, _ = oracle_rows(ixi, b, rows, topk)
+        for j, i in enumerate(rows):
+            t = ixi.q_pos0 + i
+            H.check_ascending_padded(got[b, i], min(t, ixi.k.shape[1] - 1), topk)
+            n = min(t + 1, ixi.k.shape[1])
+            msg = H.check_index_set(got[b, i], ref[j], I[j, :n], topk)
+            assert msg is None, f"batch {b} row {i}: {msg}"
+    return got
+
+
+# --------------------------------------------------------------------------- config 1
+def test_c1_tiny_fp32_exact(dsa, dev):
+    c = syn.CONFIGS[1]
+    ixi = syn.indexer_inputs(n_q=c["L"], H=c["H"], d=c["d"], dtype=syn.F32, values="int",
+                             w_dist="pow2", seed=c["seed"], device=dev)
+    check_exact(dsa, ixi, c["topk"])
+    # materialised scores equal the oracle's exactly
+    sc = dsa.indexer_scores(ixi.q, ixi.k, ixi.w).cpu().numpy()[0]
+    q, k, w = H.indexer_f64(ixi)
+    I, _ = oracle.indexer_scores(q, k, w)
+    assert np.array_equal(sc.astype(np.float64), I)
+
+
+# --------------------------------------------------------------------------- fused prefill
+@pytest.mark.parametrize("dtype", [syn.BF16, syn.FP8])
+@pytest.mark.parametrize("L,topk", [(700, 64), (3500, 128), (5000, 2048)])
+def test_fused_prefill_integer_exact(dsa, dev, dtype, L, topk):
+    """Integer-valued q, k and power-of-two w: every score is exact in fp32, so
+    the selection (with many ties) must equal the oracle's bit for bit.  L spans
+    many 64-key tiles with a ragged tail; L=3500 and 5000 exercise the
+    candidate-buffer compaction."""
+    ixi = syn.indexer_inputs(B=2, n_q=L, dtype=dtype, values="int", w_dist="pow2", seed=L + topk, device=dev)
+    rows = sample_rows(L, topk, seed=L)
+    check_exact(dsa, ixi, topk, rows=rows)
+
+
+@pytest.mark.parametrize("dtype", [syn.BF16, syn.FP8])
+def test_fused_prefill_float(dsa, dev, dtype):
+    L, topk = 4100, 2048
+    ixi = syn.indexer_inputs(B=1, n_q=L, dtype=dtype, values="normal", w_dist="u8", seed=7, device=dev)
+    check_float(dsa, ixi, topk, sample_rows(L, topk, seed=3))
+
+
+def test_fused_prefill_small_heads_and_dims(dsa, dev):
+    for H_, d, dt in ((16, 64, syn.BF16), (40, 32, syn.BF16), (64, 64, syn.FP8), (1, 128, syn.FP8)):
+        ixi = syn.indexer_inputs(B=1, n_q=333, H=H_, d=d, dtype=dt, values="int", w_dist="pow2", seed=H_ + d,
+                                 device=dev)
+        check_exact(dsa, ixi, 50)
+
+
+def test_fused_prefill_signed_weights_and_offset(dsa, dev):
+    """Signed w (negative heads) and a query window that starts at q_pos0 > 0
+    (chunked prefill: the keys before the window are already cached)."""
+    ixi = syn.indexer_inputs(B=2, n_q=300, n_k=1200, q_pos0=900, dtype=syn.BF16, values="int",
+                             w_dist="pm_pow2", seed=11, device=dev)
+    check_exact(dsa, ixi, 256)
+
+
+# --------------------------------------------------------------------------- materialised paths
+@pytest.mark.parametrize("dtype", [syn.BF16, syn.FP8])
+def test_indexer_scores_window(dsa, dev, dtype):
+    ixi = syn.indexer_inputs(B=2, n_q=600, dtype=dtype, values="normal", w_dist="normal", seed=5, device=dev)
+    row0, rows = 123, 77
+    sc = dsa.indexer_scores(ixi.q, ixi.k, ixi.w, q_scale=ixi.q_scale, k_scale=ixi.k_scale,
+                            row0=row0, rows=rows).cpu().numpy()
+    for b in range(2):
+        q, k, w = H.indexer_f64(ixi, b)
+        I, A = oracle.indexer_scores(q, k, w, rows=np.arange(row0, row0 + rows))
+        fin = np.isfinite(I)
+        assert np.array_equal(np.isfinite(sc[b]), fin)
+        err = np.abs(sc[b][fin] - I[fin])
+        assert (err <= H.SCORE_RTOL * A[fin] + 1e-30).all(), float((err / np.maximum(A[fin], 1e-30)).max())
+
+
+def test_indexer_scores_integer_exact(dsa, dev):
+    ixi = syn.indexer_inputs(B=1, n_q=500, dtype=syn.FP8, values="int", w_dist="pm_pow2", seed=6, device=dev)
+    sc = dsa.indexer_scores(ixi.q, ixi.k, ixi.w, q_scale=ixi.q_scale, k_scale=ixi.k_scale).cpu().numpy()[0]
+    q, k, w = H.indexer_f64(ixi)
+    I, _ = oracle.indexer_scores(q, k, w)
+    assert np.array_equal(sc.astype(np.float64), I)
+
+
+def test_select_from_given_scores_with_ties(dsa, dev):
+    """dsa_topk over caller scores: heavy ties (small integers), +-0.0 and long
+    rows; both sides decide on the same fp32 values, so the result is exact."""
+    g = torch.Generator(device=dev).manual_seed(9)
+    B, n_q, n_k, topk = 2, 40, 9000, 700
+    sc = torch.randint(-3, 4, (B, n_q, n_k), generator=g, device=dev).float()
+    sc[0, 5] = 0.0
+    sc[0, 6] = -0.0
+    sc[1, 7] = torch.where(torch.arange(n_k, device=dev) % 2 == 0, torch.tensor(-0.0, device=dev),
+                           torch.tensor(0.0, device=dev))
+    sc[1, 8] = torch.randn(n_k, generator=g, device=dev)
+    q_pos0 = n_k - n_q - 5
+    dummy_q = torch.zeros((B, n_q, 1, 32), dtype=torch.bfloat16, device=dev)
+    dummy_k = torch.zeros((B, n_k, 32), dtype=torch.bfloat16, device=dev)
+    dummy_w = torch.zeros((B, n_q, 1), device=dev)
+    got = dsa.topk(dummy_q, dummy_k, dummy_w, topk, q_pos0=q_pos0, scores=sc).cpu().numpy()
+    s64 = sc.cpu().double().numpy()
+    for b in range(B):
+        for i in range(n_q):
+            n = min(q_pos0 + i + 1, n_k)
+            ref = oracle.topk_row(s64[b, i, :n], topk)
+            assert np.array_equal(got[b, i], ref), (b, i)
+
+
+# --------------------------------------------------------------------------- decode scan
+@pytest.mark.parametrize("dtype", [syn.FP8, syn.BF16])
+def test_decode_scan_integer_exact_and_matches_prefill_row(dsa, dev, dtype):
+    S, topk = 6000, 2048
+    pre = syn.indexer_inputs(B=3, n_q=S, dtype=dtype, values="int", w_dist="pm_pow2", seed=21, device=dev)
+    dec = syn.IndexerInputs(dtype=dtype, q=pre.q[:, S - 1:].contiguous(), k=pre.k, w=pre.w[:, S - 1:].contiguous(),
+                            q_scale=None if pre.q_scale is None else pre.q_scale[:, S - 1:].contiguous(),
+                            k_scale=pre.k_scale, q_pos0=S - 1)
+    got_dec = check_exact(dsa, dec, topk)
+    got_pre = run_topk(dsa, pre, topk).cpu().numpy()
+    assert np.array_equal(got_dec[:, 0], got_pre[:, S - 1])
+
+
+def test_decode_scan_float_signed_w(dsa, dev):
+    ixi = syn.c5_layer_indexer(0, B=4, S=7000, device=dev)
+    check_float(dsa, ixi, 2048, np.array([0]))
+
+
+def test_decode_full_size_c5_layer(dsa, dev):
+    """One decode F layer at full size: B=8 sequences, 204800 cached fp8 keys."""
+    ixi = syn.c5_layer_indexer(0, device=dev)
+    check_float(dsa, ixi, 2048, np.array([0]))
+    ixi = syn.c5_layer_indexer(1, device=dev, values="int")
+    check_exact(dsa, ixi, 2048)
+
+
+def test_determinism(dsa, dev):
+    ixi = syn.indexer_inputs(B=1, n_q=3000, dtype=syn.BF16, values="normal", seed=4, device=dev)
+    a = run_topk(dsa, ixi, 2048)
+    b = run_topk(dsa, ixi, 2048)
+    assert torch.equal(a, b)
