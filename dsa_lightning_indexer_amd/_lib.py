@@ -2,6 +2,11 @@
 import ctypes
 import os
 
+# torch ships its own HIP runtime (SONAME libamdhip64.so.7).  Load it before
+# libdsa.so so that the library's NEEDED entry resolves to that same copy: a
+# process must not hold two HIP/HSA runtimes.
+import torch  # noqa: F401
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdsa.so")
 
