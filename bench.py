@@ -1,0 +1,283 @@
+"""Benchmark of the DSA step with IndexCache reuse on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  * prefill stack: L = 131072 tokens, 8 layers, pattern FSSSFSSS, k = 2048,
+    bf16 indexer (64 heads x 128), 16-head MLA sparse attention (576/512 latent);
+  * decode stack:  8 sequences x 204800 cached tokens, 47 layers, F at layers
+    1,5,...,45 (12 F), fp8 indexer K cache, 16-head MLA sparse decode attention.
+Both stacks go through indexcache_forward (the C ABI), inputs resident in HBM.
+
+Prints one JSON line.  `value` is indexer+Top-k score-pairs per second of the
+whole step (causal pairs scored by every F layer of both stacks / step time);
+sparse-attention tokens per second are reported beside it.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "indexer+Top-k score-pairs/s & sparse-attn tokens/s at 128K-200K; % MFMA/HBM peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=1)
+    p.add_argument("--prefill-len", type=int, default=131072)
+    p.add_argument("--decode-len", type=int, default=204800)
+    p.add_argument("--decode-batch", type=int, default=8)
+    p.add_argument("--decode-layers", type=int, default=47)
+    p.add_argument("--kernel-reps", type=int, default=5)
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-report", action="store_true", help="skip the all-F comparison and overlap matrix")
+    return p.parse_args()
+
+
+def prefill_stack(dsa, syn, L, pattern, topk, dev):
+    layers = syn.c4_stack(L=L, n_layers=len(pattern), seed=4, device=dev)
+    specs = []
+    for l, (ix, sa) in enumerate(layers):
+        spec = {"sa": {"q": sa.q, "kv": sa.kv, "scale": sa.scale, "d_v": 512,
+                       "out": torch.empty((1, L, 16, 512), dtype=torch.float32, device=dev)}}
+        if pattern[l] == "F":
+            spec["ix"] = {"q": ix.q, "k": ix.k, "w": ix.w}
+            spec["idx_out"] = torch.empty((1, L, topk), dtype=torch.int32, device=dev)
+        specs.append(spec)
+    return layers, specs
+
+
+def decode_stack(dsa, syn, B, S, n_layers, topk, dev):
+    pattern = syn.uniform_pattern(n_layers, 4)
+    specs = []
+    for l, c in enumerate(pattern):
+        sa = syn.c5_layer_sa(l, B=B, S=S, device=dev)
+        spec = {"sa": {"q": sa.q, "kv": sa.kv, "scale": sa.scale, "d_v": 512,
+                       "out": torch.empty((B, 1, 16, 512), dtype=torch.float32, device=dev)}}
+        if c == "F":
+            ix = syn.c5_layer_indexer(l, B=B, S=S, device=dev)
+            spec["ix"] = {"q": ix.q, "k": ix.k, "w": ix.w, "q_scale": ix.q_scale, "k_scale": ix.k_scale,
+                          "q_pos0": ix.q_pos0}
+            spec["idx_out"] = torch.empty((B, 1, topk), dtype=torch.int32, device=dev)
+        specs.append(spec)
+    return pattern, specs
+
+
+def time_launches(fn, reps):
+    """Average duration of fn() with HIP events on torch's current stream (the
+    stream the library launches on)."""
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record(st)
+        fn()
+        b.record(st)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def cpu_baseline(ix, topk, seconds):
+    """The oracle as it stands, on host cores, over a bounded sample of query rows
+    of the prefill stack's first F layer (rows spread over the causal range)."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    L = ix.q.shape[1]
+    qraw = ix.q[0].detach().cpu().view(torch.int16).numpy().view(np.uint16)
+    kraw = ix.k[0].detach().cpu().view(torch.int16).numpy().view(np.uint16)
+    k64 = oracle.dequantize(kraw, "bf16")
+    w64 = ix.w[0].detach().cpu().double().numpy()
+    rng = np.random.default_rng(0)
+    order = rng.permutation(L)
+    pairs = 0
+    rows = 0
+    t0 = time.perf_counter()
+    for i in order:
+        q64 = oracle.dequantize(qraw[i:i + 1], "bf16")
+        oracle.indexer_topk(q64, k64, w64[i:i + 1], topk, q_pos0=int(i))
+        pairs += int(i) + 1
+        rows += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": pairs / dt, "unit": "score-pairs/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows} random query rows of the L={L} bf16 F layer (indexer + Top-k k={topk}), "
+                      f"{pairs} causal pairs in {dt:.1f} s, float64 NumPy"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import dsa_lightning_indexer_amd as dsa
+    from synth import inputs as syn
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    topk = 2048
+    L = args.prefill_len
+    pattern_p = "FSSSFSSS"
+    t0 = time.time()
+    players, pspecs = prefill_stack(dsa, syn, L, pattern_p, topk, dev)
+    B, S = args.decode_batch, args.decode_len
+    pattern_d, dspecs = decode_stack(dsa, syn, B, S, args.decode_layers, topk, dev)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f} s; "
+        f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB resident")
+
+    ws_p = torch.empty(max(dsa.indexcache_forward_workspace_size(pattern_p, pspecs, topk), 256),
+                       dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(max(dsa.indexcache_forward_workspace_size(pattern_d, dspecs, topk), 256),
+                       dtype=torch.uint8, device=dev)
+
+    def step():
+        dsa.indexcache_forward(pattern_p, pspecs, topk, ws=ws_p)
+        dsa.indexcache_forward(pattern_d, dspecs, topk, ws=ws_d)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(st)
+    for i in range(args.steps):
+        step()
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    log(f"timed {args.steps} steps: {ms_step:.2f} ms/step (wall {wall:.2f} s)")
+
+    # phase times (same calls, events per phase)
+    ms_prefill = sum(time_launches(lambda: dsa.indexcache_forward(pattern_p, pspecs, topk, ws=ws_p), 2)) / 2
+    ms_decode = sum(time_launches(lambda: dsa.indexcache_forward(pattern_d, dspecs, topk, ws=ws_d), 3)) / 3
+
+    # dominant kernel: the fused indexer+Top-k launch of an F prefill layer
+    ix0 = players[0][0]
+    idx_tmp = pspecs[0]["idx_out"]
+    ktimes = time_launches(lambda: dsa.topk(ix0.q, ix0.k, ix0.w, topk, out=idx_tmp), args.kernel_reps)
+    k_ms = sum(ktimes) / len(ktimes)
+    pairs_layer = L * (L + 1) // 2
+    flop_layer = pairs_layer * 2 * 64 * 128
+    achieved_tflops = flop_layer / (k_ms * 1e-3) / 1e12
+    log(f"fused indexer+Top-k L={L}: {k_ms:.2f} ms/launch, {achieved_tflops:.1f} TFLOP/s")
+
+    # decode F-layer indexer+Top-k (scan + select) and one decode attention layer
+    dF = [i for i, c in enumerate(pattern_d) if c == "F"][0]
+    dix = dspecs[dF]["ix"]
+    dtimes = time_launches(lambda: dsa.topk(dix["q"], dix["k"], dix["w"], topk, q_scale=dix["q_scale"],
+                                            k_scale=dix["k_scale"], q_pos0=dix["q_pos0"],
+                                            out=dspecs[dF]["idx_out"]), args.kernel_reps)
+    d_ms = sum(dtimes) / len(dtimes)
+    scan_bytes = B * S * (128 + 4)
+
+    n_f_p = pattern_p.count("F")
+    n_f_d = pattern_d.count("F")
+    pairs_step = n_f_p * pairs_layer + n_f_d * B * S
+    sa_tokens_step = len(pattern_p) * L + len(pattern_d) * B
+    value = pairs_step / (ms_step * 1e-3)
+
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "score-pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"IndexCache DSA step: prefill stack L={L} x {len(pattern_p)} layers {pattern_p} "
+                        f"(bf16 indexer H_I=64 d_I=128, k={topk}, MLA sparse attention 16 heads 576/512) + "
+                        f"decode stack B={B} x S={S} x {len(pattern_d)} layers FSSS ({n_f_d} F, fp8 indexer "
+                        f"K cache, k={topk})",
+            "prefill_len": L, "decode_batch": B, "decode_len": S, "topk": topk,
+        },
+        "sparse_attn_tokens_per_s": sa_tokens_step / (ms_step * 1e-3),
+        "phases": {
+            "prefill_stack_ms": ms_prefill,
+            "decode_stack_ms": ms_decode,
+            "decode_tokens_per_s": B / (ms_decode * 1e-3),
+            "prefill_indexer_topk_ms_per_F_layer": k_ms,
+            "decode_indexer_topk_ms_per_F_layer": d_ms,
+            "decode_scan_select_hbm_GBs": scan_bytes / (d_ms * 1e-3) / 1e9,
+        },
+        "roofline": {
+            "kernel": "fused indexer+Top-k (prefill, bf16)",
+            "bound": "mfma",
+            "achieved": achieved_tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved_tflops / PEAK_BF16_TFLOPS,
+            "traffic": None,
+            "algorithmic_per_launch": f"{pairs_layer} causal pairs x 16384 flop = {flop_layer:.4g} flop",
+            "launch_ms": k_ms,
+        },
+    }
+
+    if not args.no_report:
+        # S-vs-F: the same stack with every layer F, plus the all-F overlap matrix
+        pattern_f = "F" * len(pattern_p)
+        fspecs = []
+        for l, (ix, sa) in enumerate(players):
+            fspecs.append({"ix": {"q": ix.q, "k": ix.k, "w": ix.w}, "sa": pspecs[l]["sa"],
+                           "idx_out": pspecs[l].get("idx_out") if pattern_p[l] == "F" else
+                           torch.empty((1, L, topk), dtype=torch.int32, device=dev)})
+        ws_f = torch.empty(max(dsa.indexcache_forward_workspace_size(pattern_f, fspecs, topk), 256),
+                           dtype=torch.uint8, device=dev)
+        ms_allf = time_launches(lambda: dsa.indexcache_forward(pattern_f, fspecs, topk, ws=ws_f), 1)[0]
+        sa0 = pspecs[1]["sa"]
+        sa_ms = sum(time_launches(lambda: dsa.sparse_attn(sa0["q"], sa0["kv"], pspecs[0]["idx_out"],
+                                                          sa0["scale"], d_v=512, out=sa0["out"]), 2)) / 2
+        rows = L - topk + 1
+        M = [[1.0] * len(pattern_f) for _ in pattern_f]
+        for i in range(len(pattern_f)):
+            for j in range(i + 1, len(pattern_f)):
+                tot = dsa.index_overlap(fspecs[i]["idx_out"][0, topk - 1:], fspecs[j]["idx_out"][0, topk - 1:],
+                                        topk)
+                M[i][j] = M[j][i] = int(tot.item()) / (rows * topk)
+        rec["report"] = {
+            "all_F_stack_ms": ms_allf,
+            "FSSSFSSS_stack_ms": ms_prefill,
+            "stack_speedup": ms_allf / ms_prefill,
+            "F_layer_ms": k_ms + sa_ms,
+            "S_layer_ms": sa_ms,
+            "S_over_F_layer_speedup": (k_ms + sa_ms) / sa_ms,
+            "sparse_attn_prefill_ms_per_layer": sa_ms,
+            "sparse_attn_gathered_GBs": L * topk * 1152 / (sa_ms * 1e-3) / 1e9,
+            "overlap_matrix_all_F": [[round(x, 4) for x in r] for r in M],
+        }
+        log(f"all-F stack {ms_allf:.1f} ms vs FSSSFSSS {ms_prefill:.1f} ms; SA {sa_ms:.2f} ms/layer")
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        rec["cpu_baseline"] = cpu_baseline(players[0][0], topk, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -174,19 +174,23 @@ __global__ __launch_bounds__(256, 1) void sa_mla_kernel(SAParams p) {
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx);
-    bf16x4 pb;
+    // P is split into bf16 hi + lo parts (P ~= hi + lo to ~2^-17 relative) so the
+    // bf16 MFMA P.V keeps fp32-level accuracy of the softmax weights.
+    bf16x4 pb_hi, pb_lo;
     float alpha = 1.f;
     if (m_new == -__builtin_inff()) {
-      pb = bf16x4{};
+      pb_hi = bf16x4{};
+      pb_lo = bf16x4{};
     } else {
       alpha = (m_run == -__builtin_inff()) ? 0.f : __expf(m_run - m_new);
       float ps = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float pe = z[i] == -__builtin_inff() ? 0.f : __expf(z[i] - m_new);
-        const __bf16 pbh = (__bf16)pe;
-        pb[i] = pbh;
-        ps += (float)pbh;       // normalise with the same rounded weights P.V uses
+        const __bf16 hi = (__bf16)pe;
+        pb_hi[i] = hi;
+        pb_lo[i] = (__bf16)(pe - (float)hi);
+        ps += pe;
       }
       l_run = l_run * alpha + ps;
       m_run = m_new;
@@ -196,7 +200,8 @@ __global__ __launch_bounds__(256, 1) void sa_mla_kernel(SAParams p) {
     for (int dt = 0; dt < NDT; ++dt) {
       o[dt] *= alpha;
       const bf16x4 va = *(const bf16x4*)&vt[wid][16 * dt + col][4 * g];
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_hi, o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_lo, o[dt], 0, 0, 0);
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
   }
