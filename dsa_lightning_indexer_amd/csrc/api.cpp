@@ -94,7 +94,7 @@ size_t topk_ws(const dsa_indexer_args* a, const float* scores) {
     case PATH_SCAN:
       return align_up((size_t)rows * a->n_k * sizeof(float)) +
              align_up(dsa_host::select_workspace_bytes(rows));
-    case PATH_FUSED: return 0;
+    case PATH_FUSED: return align_up(dsa_host::topk_fused_ws_bytes());
   }
   return 0;
 }
@@ -126,7 +126,7 @@ dsa_status run_topk(const dsa_indexer_args* a, const float* scores, int32_t k, i
   const TopkPath path = topk_path(a, scores);
   hipError_t e = hipSuccess;
   if (path == PATH_FUSED) {
-    e = dsa_host::indexer_topk_fused(*a, k, idx, s);
+    e = dsa_host::indexer_topk_fused(*a, k, idx, ws, s);
     return hip_status(e, "fused indexer+topk launch");
   }
   const float* sc = scores;

@@ -87,7 +87,11 @@ hipError_t indexer_scores_f32(const dsa_indexer_args& a, int64_t row0, int64_t r
                               int64_t out_row_stride, hipStream_t s);
 hipError_t indexer_scores_mfma(const dsa_indexer_args& a, int64_t row0, int64_t rows, float* out,
                                hipStream_t s);
-hipError_t indexer_topk_fused(const dsa_indexer_args& a, int32_t k, int32_t* idx, hipStream_t s);
+// Fused prefill INDEXER + Top-k: persistent grid of at most kTopkSlots workgroups,
+// each with a private candidate slice in the workspace (topk_fused_ws_bytes()).
+constexpr int kTopkSlots = 512;
+size_t topk_fused_ws_bytes();
+hipError_t indexer_topk_fused(const dsa_indexer_args& a, int32_t k, int32_t* idx, void* ws, hipStream_t s);
 // Decode-shaped scan: fp32 scores of every (row, s) into `scores` [batch*n_q, n_k] and the
 // first select histogram into the select workspace `sel_ws` (already prepared).
 hipError_t indexer_scan(const dsa_indexer_args& a, float* scores, void* sel_ws, int32_t k,

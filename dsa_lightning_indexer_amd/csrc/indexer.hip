@@ -33,7 +33,6 @@ enum { MODE_SCORES = 0, MODE_TOPK = 1 };
 
 constexpr int kTileKeys = 64;
 constexpr int kRowsPerBlock = 4;       // one query row per wave
-constexpr int kCandCap = 3072;         // per-row candidate buffer (>= k + 64)
 
 struct IxParams {
   const void* q;
@@ -170,226 +169,330 @@ template <int DT, int D, int HT>
 __device__ __forceinline__ float tile_scores(const RowState<DT, D, HT>& rs, const uint8_t* kt,
                                              int pitch, int lane) {
   typedef Cfg<DT, D> C;
-  f32x16 acc[HT][2];
+  // Two 32-key subtiles, one after the other: the head-sum epilogue of the
+  // first overlaps the MFMAs of the second and only 16*HT accumulators live.
+  float part[2];
 #pragma unroll
-  for (int h = 0; h < HT; ++h) { acc[h][0] = f32x16{}; acc[h][1] = f32x16{}; }
+  for (int n = 0; n < 2; ++n) {
+    f32x16 acc[HT];
 #pragma unroll
-  for (int ks = 0; ks < C::NKS; ++ks) {
+    for (int h = 0; h < HT; ++h) acc[h] = f32x16{};
+    const uint8_t* rowp = kt + (32 * n + (lane & 31)) * pitch;
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      typename AFrag<DT>::T bf = load_frag<DT>(kt + (32 * n + (lane & 31)) * pitch, ks, lane);
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      typename AFrag<DT>::T bf = load_frag<DT>(rowp, ks, lane);
 #pragma unroll
-      for (int h = 0; h < HT; ++h) acc[h][n] = mfma<DT>(rs.a[h][ks], bf, acc[h][n]);
+      for (int h = 0; h < HT; ++h) acc[h] = mfma<DT>(rs.a[h][ks], bf, acc[h]);
     }
-  }
-  // 32x32 output: lane l holds column (key) l%32 and rows 8*(i/4) + 4*(l/32) + i%4.
-  float p0 = 0.f, p1 = 0.f;
+    // 32x32 output: lane l holds column (key) l%32 and rows 8*(i/4) + 4*(l/32) + i%4.
+    float pp = 0.f;
 #pragma unroll
-  for (int h = 0; h < HT; ++h) {
+    for (int h = 0; h < HT; ++h) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      p0 = fmaf(rs.c[h][i], fmaxf(acc[h][0][i], 0.f), p0);
-      p1 = fmaf(rs.c[h][i], fmaxf(acc[h][1][i], 0.f), p1);
+      for (int i = 0; i < 16; ++i) pp = fmaf(rs.c[h][i], fmaxf(acc[h][i], 0.f), pp);
     }
+    part[n] = pp;
   }
   // lanes l and l^32 hold complementary head rows of the same key column:
   // lanes 0-31 finish keys 0-31 (subtile 0), lanes 32-63 keys 32-63 (subtile 1).
   const bool lo = lane < 32;
-  const float send = lo ? p1 : p0;
+  const float send = lo ? part[1] : part[0];
   const float recv = __shfl_xor(send, 32, 64);
-  return (lo ? p0 : p1) + recv;
+  return (lo ? part[0] : part[1]) + recv;
+}
+
+// Cooperative 256-thread copy of the 64-key tile `tile` into registers, then LDS
+// (rows of PITCH bytes).  Keys at or past n_k read as zero.
+template <int DT, int D>
+__device__ __forceinline__ void load_ktile(const uint8_t* kbase, int64_t n_k, int tile,
+                                           i32x4 (&pre)[Cfg<DT, D>::NCH]) {
+  typedef Cfg<DT, D> C;
+#pragma unroll
+  for (int j = 0; j < C::NCH; ++j) {
+    const int c = threadIdx.x + 256 * j;
+    const int key = c / C::CPR, part = c % C::CPR;
+    const int64_t s = (int64_t)tile * kTileKeys + key;
+    pre[j] = s < n_k ? *(const i32x4*)(kbase + s * C::ROWB + part * 16) : i32x4{};
+  }
+}
+template <int DT, int D>
+__device__ __forceinline__ void store_ktile(uint8_t* dst, const i32x4 (&pre)[Cfg<DT, D>::NCH]) {
+  typedef Cfg<DT, D> C;
+#pragma unroll
+  for (int j = 0; j < C::NCH; ++j) {
+    const int c = threadIdx.x + 256 * j;
+    const int key = c / C::CPR, part = c % C::CPR;
+    *(i32x4*)(&dst[key * C::PITCH + part * 16]) = pre[j];
+  }
 }
 
 // ---------------------------------------------------------------- wave select
+// A wave owns one query row's candidate buffer (order keys cu[], positions ci[])
+// in a private slice of the workspace.  Entries are appended in position order.
 __device__ __forceinline__ void lds_sync() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup"); }
 
-// k-th largest key T among cu[0..n) and how many entries equal to T are kept.
-__device__ void wave_radix_select(const uint32_t* cu, int n, int k, uint32_t* hist, int lane,
-                                  uint32_t& T, uint32_t& req) {
-  uint32_t prefix = 0, mask = 0, rem = (uint32_t)k;
-#pragma unroll 1
-  for (int shift = 24; shift >= 0; shift -= 8) {
+constexpr int kCandCap = 16384;        // candidates per row before a compaction
+
+// One radix pass: histogram of the 8-bit digit at `shift` among entries whose
+// masked key equals `prefix`; then pick the digit holding the rem-th largest.
+// Returns the digit; rem becomes the rank inside that digit's bucket and
+// *bucket the bucket's size.
+__device__ uint32_t wave_radix_pass(const uint32_t* cu, int n, uint32_t prefix, uint32_t mask, int shift,
+                                    uint32_t& rem, uint32_t* bucket, uint32_t* hist, int lane) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) hist[lane * 4 + j] = 0u;
-    lds_sync();
-    for (int j = lane; j < n; j += 64) {
-      uint32_t u = cu[j];
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+  for (int j = 0; j < 4; ++j) hist[lane * 4 + j] = 0u;
+  lds_sync();
+  for (int j0 = 0; j0 < n; j0 += 64 * 8) {
+    uint32_t u[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int j = j0 + r * 64 + lane;
+      u[r] = j < n ? cu[j] : 0u;
     }
-    lds_sync();
-    // lane owns bins 255-4*lane .. 252-4*lane (descending order)
-    uint32_t c0 = hist[255 - 4 * lane], c1 = hist[254 - 4 * lane];
-    uint32_t c2 = hist[253 - 4 * lane], c3 = hist[252 - 4 * lane];
-    uint32_t local = c0 + c1 + c2 + c3, tot;
-    uint32_t ex = wave_excl_scan(local, &tot);
-    bool mine = ex < rem && rem <= ex + local;
-    uint32_t digit = 0, nrem = 0;
-    if (mine) {
-      uint32_t cc = ex;
-      uint32_t cs[4] = {c0, c1, c2, c3};
-      for (int j = 0; j < 4; ++j) {
-        if (cc + cs[j] >= rem) { digit = 255u - 4u * lane - j; nrem = rem - cc; break; }
-        cc += cs[j];
-      }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int j = j0 + r * 64 + lane;
+      if (j < n && (u[r] & mask) == prefix) atomicAdd(&hist[(u[r] >> shift) & 255u], 1u);
     }
-    uint64_t m = ballot(mine);
-    int src = __builtin_ctzll(m);
-    digit = __shfl(digit, src, 64);
-    nrem = __shfl(nrem, src, 64);
-    prefix |= digit << shift;
-    mask |= 0xFFu << shift;
-    rem = nrem;
-    lds_sync();
   }
-  T = prefix;
-  req = rem;
+  lds_sync();
+  // lane owns bins 255-4*lane .. 252-4*lane (descending)
+  const uint32_t c0 = hist[255 - 4 * lane], c1 = hist[254 - 4 * lane];
+  const uint32_t c2 = hist[253 - 4 * lane], c3 = hist[252 - 4 * lane];
+  const uint32_t local = c0 + c1 + c2 + c3;
+  uint32_t tot;
+  const uint32_t ex = wave_excl_scan(local, &tot);
+  const bool mine = ex < rem && rem <= ex + local;
+  uint32_t digit = 0, nrem = 0, bsz = 0;
+  if (mine) {
+    uint32_t cc = ex;
+    const uint32_t cs[4] = {c0, c1, c2, c3};
+    for (int j = 0; j < 4; ++j) {
+      if (cc + cs[j] >= rem) { digit = 255u - 4u * lane - j; nrem = rem - cc; bsz = cs[j]; break; }
+      cc += cs[j];
+    }
+  }
+  const int src = __builtin_ctzll(ballot(mine));
+  digit = __shfl(digit, src, 64);
+  rem = __shfl(nrem, src, 64);
+  *bucket = __shfl(bsz, src, 64);
+  lds_sync();
+  return digit;
 }
 
-// Keep the top k of cu/ci[0..n) in position order.  Writes to (du, di) which may
-// alias (cu, ci) (in-place, stable).  Returns the number kept (== k when n >= k).
-__device__ int wave_compact(uint32_t* cu, uint32_t* ci, int n, uint32_t T, uint32_t req, int lane,
-                            uint32_t* du, int32_t* di_global, uint32_t* di_lds, int limit) {
+// Stable in-place compaction of cu/ci[0..n): keeps entries with key > T, plus
+// (when tie_limit >= 0) the first tie_limit entries with key == T, or (when
+// tie_limit < 0) every entry with key == T.  With out_idx set, the kept
+// positions go there instead (at most `limit`).  Returns the number kept.
+__device__ int wave_keep(uint32_t* cu, uint32_t* ci, int n, uint32_t T, int64_t tie_limit, int lane,
+                         int32_t* out_idx, int limit) {
   int out = 0;
-  uint32_t eqseen = 0;
-  for (int j0 = 0; j0 < n; j0 += 64) {
-    const int j = j0 + lane;
-    const bool in = j < n;
-    const uint32_t u = in ? cu[j] : 0u;
-    const uint32_t id = in ? ci[j] : 0u;
-    const bool tie = in && u == T;
-    const uint64_t tm = ballot(tie);
-    const uint32_t trank = eqseen + lanes_below(tm);
-    const bool keep = in && (u > T || (tie && trank < req));
-    eqseen += (uint32_t)__builtin_popcountll(tm);
-    const uint64_t km = ballot(keep);
-    if (keep) {
-      const int d = out + (int)lanes_below(km);
-      if (di_global) {
-        if (d < limit) di_global[d] = (int32_t)id;
-      } else if (d < limit) {
-        du[d] = u;
-        di_lds[d] = id;
-      }
+  int64_t eqseen = 0;
+  for (int j0 = 0; j0 < n; j0 += 64 * 4) {
+    uint32_t u[4], id[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = j0 + r * 64 + lane;
+      u[r] = j < n ? cu[j] : 0u;
+      id[r] = j < n ? ci[j] : 0u;
     }
-    out += __builtin_popcountll(km);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = j0 + r * 64 + lane;
+      const bool in = j < n;
+      const bool tie = in && u[r] == T;
+      const uint64_t tm = ballot(tie);
+      const int64_t trank = eqseen + lanes_below(tm);
+      const bool keep = in && (u[r] > T || (tie && (tie_limit < 0 || trank < tie_limit)));
+      eqseen += __builtin_popcountll(tm);
+      const uint64_t km = ballot(keep);
+      if (keep) {
+        const int d = out + (int)lanes_below(km);
+        if (out_idx) {
+          if (d < limit) out_idx[d] = (int32_t)id[r];
+        } else if (d < limit) {
+          cu[d] = u[r];
+          ci[d] = id[r];
+        }
+      }
+      out += __builtin_popcountll(km);
+    }
   }
   lds_sync();
   return out;
 }
 
-// ---------------------------------------------------------------- prefill kernel
-template <int DT, int D, int HT, int MODE>
-__global__ __launch_bounds__(256, 1) void ix_tile_kernel(IxParams p) {
+// Exact k-th largest key T among cu[0..n) and how many entries equal to T fit.
+__device__ void wave_select_exact(const uint32_t* cu, int n, int k, uint32_t* hist, int lane, uint32_t& T,
+                                  uint32_t& req) {
+  uint32_t prefix = 0, mask = 0, rem = (uint32_t)k, bucket;
+#pragma unroll 1
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    const uint32_t d = wave_radix_pass(cu, n, prefix, mask, shift, rem, &bucket, hist, lane);
+    prefix |= d << shift;
+    mask |= 0xFFu << shift;
+  }
+  T = prefix;
+  req = rem;
+}
+
+// Shrink a full buffer while keeping every entry that can still be in the row's
+// Top-k.  First try the 16-bit prefix of the k-th key (two passes): keep every
+// entry at or above it; new arrivals must then be >= that prefix.  If ties or a
+// crowded bucket leave the buffer too full, select exactly (k entries kept,
+// arrivals must beat T strictly: a later position loses a tie).
+__device__ int wave_shrink(uint32_t* cu, uint32_t* ci, int n, int k, uint32_t* hist, int lane,
+                           uint32_t& thr, bool& strict) {
+  uint32_t rem = (uint32_t)k, bucket;
+  const uint32_t d1 = wave_radix_pass(cu, n, 0u, 0u, 24, rem, &bucket, hist, lane);
+  const uint32_t d2 = wave_radix_pass(cu, n, d1 << 24, 0xFF000000u, 16, rem, &bucket, hist, lane);
+  const uint32_t P = (d1 << 24) | (d2 << 16);
+  const int kept = (k - (int)rem) + (int)bucket;          // entries with key >= P
+  if (kept <= n - n / 4) {
+    const int m = wave_keep(cu, ci, n, P, -1, lane, nullptr, n);   // key > P or == P ...
+    // wave_keep with tie_limit < 0 keeps key >= P exactly; entries in (P, P+0xFFFF] are > P.
+    thr = P;
+    strict = false;
+    return m;
+  }
+  uint32_t T, req;
+  wave_select_exact(cu, n, k, hist, lane, T, req);
+  const int m = wave_keep(cu, ci, n, T, (int64_t)req, lane, nullptr, n);
+  thr = T;
+  strict = true;
+  return m;
+}
+
+// ---------------------------------------------------------------- prefill kernels
+// Scores mode: materialise I for a window of query rows (-inf where s > t).
+template <int DT, int D, int HT>
+__global__ __launch_bounds__(256, 2) void ix_scores_kernel(IxParams p) {
   typedef Cfg<DT, D> C;
   __shared__ __attribute__((aligned(16))) uint8_t ktile[2][C::TILE_BYTES];
-  __shared__ uint32_t cand_u[MODE == MODE_TOPK ? kRowsPerBlock : 1][MODE == MODE_TOPK ? kCandCap : 1];
-  __shared__ uint32_t cand_i[MODE == MODE_TOPK ? kRowsPerBlock : 1][MODE == MODE_TOPK ? kCandCap : 1];
-  __shared__ uint32_t hist[MODE == MODE_TOPK ? kRowsPerBlock : 1][256];
-
   const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t nrb = (p.rows + kRowsPerBlock - 1) / kRowsPerBlock;
   const int b = (int)(blockIdx.x % p.batch);
-  const int64_t rb = nrb - 1 - (int64_t)(blockIdx.x / p.batch);   // heaviest rows first
-  const int64_t rloc0 = rb * kRowsPerBlock;                          // within the window
-  const int64_t rloc = rloc0 + wid;
+  const int64_t rloc = (int64_t)(blockIdx.x / p.batch) * kRowsPerBlock + wid;
   const bool vrow = rloc < p.rows;
-  const int64_t i = p.row0 + rloc;                                   // query row
+  const int64_t i = p.row0 + rloc;
   const int64_t t = p.q_pos0 + i;
-  const int64_t rlast = (rloc0 + kRowsPerBlock - 1 < p.rows ? rloc0 + kRowsPerBlock - 1 : p.rows - 1);
-  const int64_t t_last = p.q_pos0 + p.row0 + rlast;
-  int64_t nkeys;
-  if (MODE == MODE_SCORES) nkeys = p.n_k;
-  else nkeys = t_last + 1 < p.n_k ? t_last + 1 : p.n_k;
-  const int ntiles = (int)((nkeys + kTileKeys - 1) / kTileKeys);
+  const int ntiles = (int)((p.n_k + kTileKeys - 1) / kTileKeys);
   const int64_t gi = (int64_t)b * p.n_q + i;
-
   RowState<DT, D, HT> rs;
   if (vrow) load_row<DT, D, HT>(p, gi, lane, rs);
-
   const uint8_t* kbase = (const uint8_t*)p.k + (int64_t)b * p.k_bs * C::ES;
   const float* ksc = (DT == DT_FP8) ? p.k_scale + (int64_t)b * p.ks_bs : nullptr;
-
   i32x4 pre[C::NCH];
-  auto gload = [&](int tile) {
-#pragma unroll
-    for (int j = 0; j < C::NCH; ++j) {
-      const int c = threadIdx.x + 256 * j;
-      const int key = c / C::CPR, part = c % C::CPR;
-      const int64_t s = (int64_t)tile * kTileKeys + key;
-      pre[j] = s < p.n_k ? *(const i32x4*)(kbase + s * C::ROWB + part * 16) : i32x4{};
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < C::NCH; ++j) {
-      const int c = threadIdx.x + 256 * j;
-      const int key = c / C::CPR, part = c % C::CPR;
-      *(i32x4*)(&ktile[buf][key * C::PITCH + part * 16]) = pre[j];
-    }
-  };
-
-  // candidate state (MODE_TOPK)
-  int cnt = 0;
-  bool full = false;
-  uint32_t thr = 0;
-  const int k = p.topk;
-
-  if (ntiles > 0) { gload(0); lstore(0); }
+  load_ktile<DT, D>(kbase, p.n_k, 0, pre);
+  store_ktile<DT, D>(ktile[0], pre);
   for (int it = 0; it < ntiles; ++it) {
     __syncthreads();
-    if (it + 1 < ntiles) gload(it + 1);
-    const int64_t s0 = (int64_t)it * kTileKeys;
-    if (vrow && (MODE == MODE_SCORES || s0 <= t)) {
+    if (it + 1 < ntiles) load_ktile<DT, D>(kbase, p.n_k, it + 1, pre);
+    if (vrow) {
       float sc = tile_scores<DT, D, HT>(rs, &ktile[it & 1][0], C::PITCH, lane);
-      const int64_t s = s0 + lane;
-      if constexpr (DT == DT_FP8) {
-        if (s < p.n_k) sc *= ksc[s];
+      const int64_t s = (int64_t)it * kTileKeys + lane;
+      if (s < p.n_k) {
+        if constexpr (DT == DT_FP8) sc *= ksc[s];
+        float* out = p.out + ((int64_t)b * p.rows + rloc) * p.n_k;
+        out[s] = s <= t ? sc + 0.0f : -__builtin_inff();
       }
-      const bool valid = s <= t && s < p.n_k;
-      if constexpr (MODE == MODE_SCORES) {
-        if (s < p.n_k) {
-          float* out = p.out + ((int64_t)b * p.rows + rloc) * p.n_k;
-          out[s] = valid ? sc + 0.0f : -__builtin_inff();
+    }
+    if (it + 1 < ntiles) store_ktile<DT, D>(ktile[(it + 1) & 1], pre);
+  }
+}
+
+// Fused INDEXER + Top-k.  Persistent: each workgroup repeatedly takes the next
+// block of 4 query rows (heaviest rows first) from a device counter; blockIdx.x
+// names its private candidate slice in the workspace.
+template <int DT, int D, int HT>
+__global__ __launch_bounds__(256, 2) void ix_topk_kernel(IxParams p, uint32_t* work, uint32_t* cand) {
+  typedef Cfg<DT, D> C;
+  __shared__ __attribute__((aligned(16))) uint8_t ktile[2][C::TILE_BYTES];
+  __shared__ uint32_t hist[kRowsPerBlock][256];
+  __shared__ int64_t s_item;
+
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t* cu = cand + ((size_t)blockIdx.x * kRowsPerBlock + wid) * 2 * kCandCap;
+  uint32_t* ci = cu + kCandCap;
+  const int64_t nrb = (p.rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int64_t total = nrb * p.batch;
+  const int k = p.topk;
+
+  for (;;) {
+    if (threadIdx.x == 0) s_item = (int64_t)atomicAdd(work, 1u);
+    __syncthreads();
+    const int64_t item = s_item;
+    __syncthreads();
+    if (item >= total) break;
+    const int b = (int)(item % p.batch);
+    const int64_t rb = nrb - 1 - item / p.batch;                 // heaviest rows first
+    const int64_t rloc0 = rb * kRowsPerBlock;
+    const int64_t rloc = rloc0 + wid;
+    const bool vrow = rloc < p.rows;
+    const int64_t i = p.row0 + rloc;
+    const int64_t t = p.q_pos0 + i;
+    const int64_t rlast = rloc0 + kRowsPerBlock - 1 < p.rows ? rloc0 + kRowsPerBlock - 1 : p.rows - 1;
+    const int64_t t_last = p.q_pos0 + p.row0 + rlast;
+    const int64_t nkeys = t_last + 1 < p.n_k ? t_last + 1 : p.n_k;
+    const int ntiles = (int)((nkeys + kTileKeys - 1) / kTileKeys);
+    const int64_t gi = (int64_t)b * p.n_q + i;
+
+    RowState<DT, D, HT> rs;
+    if (vrow) load_row<DT, D, HT>(p, gi, lane, rs);
+    const uint8_t* kbase = (const uint8_t*)p.k + (int64_t)b * p.k_bs * C::ES;
+    const float* ksc = (DT == DT_FP8) ? p.k_scale + (int64_t)b * p.ks_bs : nullptr;
+
+    int cnt = 0;
+    bool full = false, strict = false;
+    uint32_t thr = 0;
+    i32x4 pre[C::NCH];
+    if (ntiles > 0) {
+      load_ktile<DT, D>(kbase, p.n_k, 0, pre);
+      store_ktile<DT, D>(ktile[0], pre);
+    }
+    for (int it = 0; it < ntiles; ++it) {
+      __syncthreads();
+      if (it + 1 < ntiles) load_ktile<DT, D>(kbase, p.n_k, it + 1, pre);
+      const int64_t s0 = (int64_t)it * kTileKeys;
+      if (vrow && s0 <= t) {
+        float sc = tile_scores<DT, D, HT>(rs, &ktile[it & 1][0], C::PITCH, lane);
+        const int64_t s = s0 + lane;
+        if constexpr (DT == DT_FP8) {
+          if (s < p.n_k) sc *= ksc[s];
         }
-      } else {
+        const bool valid = s <= t && s < p.n_k;
         const uint32_t u = order_key(sc);
-        const bool pred = valid && (!full || u > thr);
         if (cnt + 64 > kCandCap) {
-          uint32_t T, req;
-          wave_radix_select(cand_u[wid], cnt, k, hist[wid], lane, T, req);
-          cnt = wave_compact(cand_u[wid], cand_i[wid], cnt, T, req, lane, cand_u[wid], nullptr,
-                             cand_i[wid], kCandCap);
+          lds_sync();
+          cnt = wave_shrink(cu, ci, cnt, k, hist[wid], lane, thr, strict);
           full = true;
-          thr = T;
         }
-        const bool pr = pred && (!full || u > thr);
+        const bool pr = valid && (!full || (strict ? u > thr : u >= thr));
         const uint64_t m = ballot(pr);
         if (pr) {
           const int d = cnt + (int)lanes_below(m);
-          cand_u[wid][d] = u;
-          cand_i[wid][d] = (uint32_t)s;
+          cu[d] = u;
+          ci[d] = (uint32_t)s;
         }
         cnt += __builtin_popcountll(m);
       }
+      if (it + 1 < ntiles) store_ktile<DT, D>(ktile[(it + 1) & 1], pre);
     }
-    if (it + 1 < ntiles) lstore((it + 1) & 1);
-  }
-
-  if constexpr (MODE == MODE_TOPK) {
-    if (!vrow) return;
-    lds_sync();
-    int32_t* out = p.idx + gi * (int64_t)k;
-    int nout;
-    if (cnt > k) {
-      uint32_t T, req;
-      wave_radix_select(cand_u[wid], cnt, k, hist[wid], lane, T, req);
-      nout = wave_compact(cand_u[wid], cand_i[wid], cnt, T, req, lane, nullptr, out, nullptr, k);
-      nout = nout < k ? nout : k;
-    } else {
-      for (int j = lane; j < cnt; j += 64) out[j] = (int32_t)cand_i[wid][j];
-      nout = cnt;
+    if (vrow) {
+      lds_sync();
+      int32_t* out = p.idx + gi * (int64_t)k;
+      int nout;
+      if (cnt > k) {
+        uint32_t T, req;
+        wave_select_exact(cu, cnt, k, hist[wid], lane, T, req);
+        nout = wave_keep(cu, ci, cnt, T, (int64_t)req, lane, out, k);
+        nout = nout < k ? nout : k;
+      } else {
+        for (int j = lane; j < cnt; j += 64) out[j] = (int32_t)ci[j];
+        nout = cnt;
+      }
+      for (int j = nout + lane; j < k; j += 64) out[j] = -1;
+      lds_sync();
     }
-    for (int j = nout + lane; j < k; j += 64) out[j] = -1;
   }
 }
 
@@ -477,29 +580,52 @@ IxParams make_params(const dsa_indexer_args& a) {
   return p;
 }
 
-template <int MODE, int DT, int D>
-hipError_t launch_tile_dt(const IxParams& p, hipStream_t s) {
+template <int DT, int D>
+hipError_t launch_scores_dt(const IxParams& p, hipStream_t s) {
   const int64_t nrb = (p.rows + kRowsPerBlock - 1) / kRowsPerBlock;
   dim3 grid((unsigned)(nrb * p.batch));
   if (p.heads > 32) {
-    hipLaunchKernelGGL((ix_tile_kernel<DT, D, 2, MODE>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((ix_scores_kernel<DT, D, 2>), grid, dim3(256), 0, s, p);
   } else {
-    hipLaunchKernelGGL((ix_tile_kernel<DT, D, 1, MODE>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((ix_scores_kernel<DT, D, 1>), grid, dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }
 
-template <int MODE>
-hipError_t launch_tile(const dsa_indexer_args& a, const IxParams& p, hipStream_t s) {
-  if (a.dtype == DSA_BF16) {
-    if (a.dim == 128) return launch_tile_dt<MODE, DT_BF16, 128>(p, s);
-    if (a.dim == 64) return launch_tile_dt<MODE, DT_BF16, 64>(p, s);
-    if (a.dim == 32) return launch_tile_dt<MODE, DT_BF16, 32>(p, s);
-  } else if (a.dtype == DSA_FP8_E4M3) {
-    if (a.dim == 128) return launch_tile_dt<MODE, DT_FP8, 128>(p, s);
-    if (a.dim == 64) return launch_tile_dt<MODE, DT_FP8, 64>(p, s);
+__global__ void zero_u32_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+int persistent_blocks() {
+  static int cached = 0;
+  if (cached) return cached;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  int nb = 2 * cus;
+  if (nb > dsa_host::kTopkSlots) nb = dsa_host::kTopkSlots;
+  cached = nb;
+  return nb;
+}
+
+template <int DT, int D>
+hipError_t launch_topk_dt(const IxParams& p, void* ws, hipStream_t s) {
+  uint32_t* work = (uint32_t*)ws;
+  uint32_t* cand = (uint32_t*)((char*)ws + 256);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, s, work, 64);
+  const int64_t nrb = (p.rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  int64_t items = nrb * p.batch;
+  int64_t nb = persistent_blocks();
+  if (nb > items) nb = items;
+  dim3 grid((unsigned)nb);
+  if (p.heads > 32) {
+    hipLaunchKernelGGL((ix_topk_kernel<DT, D, 2>), grid, dim3(256), 0, s, p, work, cand);
+  } else {
+    hipLaunchKernelGGL((ix_topk_kernel<DT, D, 1>), grid, dim3(256), 0, s, p, work, cand);
   }
-  return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 template <int DT, int D>
@@ -543,14 +669,34 @@ hipError_t indexer_scores_mfma(const dsa_indexer_args& a, int64_t row0, int64_t 
   p.row0 = row0;
   p.rows = rows;
   p.out = out;
-  return launch_tile<MODE_SCORES>(a, p, s);
+  if (a.dtype == DSA_BF16) {
+    if (a.dim == 128) return launch_scores_dt<DT_BF16, 128>(p, s);
+    if (a.dim == 64) return launch_scores_dt<DT_BF16, 64>(p, s);
+    if (a.dim == 32) return launch_scores_dt<DT_BF16, 32>(p, s);
+  } else if (a.dtype == DSA_FP8_E4M3) {
+    if (a.dim == 128) return launch_scores_dt<DT_FP8, 128>(p, s);
+    if (a.dim == 64) return launch_scores_dt<DT_FP8, 64>(p, s);
+  }
+  return hipErrorInvalidValue;
 }
 
-hipError_t indexer_topk_fused(const dsa_indexer_args& a, int32_t k, int32_t* idx, hipStream_t s) {
+size_t topk_fused_ws_bytes() {
+  return 256 + (size_t)kTopkSlots * kRowsPerBlock * 2 * kCandCap * sizeof(uint32_t);
+}
+
+hipError_t indexer_topk_fused(const dsa_indexer_args& a, int32_t k, int32_t* idx, void* ws, hipStream_t s) {
   IxParams p = make_params(a);
   p.idx = idx;
   p.topk = k;
-  return launch_tile<MODE_TOPK>(a, p, s);
+  if (a.dtype == DSA_BF16) {
+    if (a.dim == 128) return launch_topk_dt<DT_BF16, 128>(p, ws, s);
+    if (a.dim == 64) return launch_topk_dt<DT_BF16, 64>(p, ws, s);
+    if (a.dim == 32) return launch_topk_dt<DT_BF16, 32>(p, ws, s);
+  } else if (a.dtype == DSA_FP8_E4M3) {
+    if (a.dim == 128) return launch_topk_dt<DT_FP8, 128>(p, ws, s);
+    if (a.dim == 64) return launch_topk_dt<DT_FP8, 64>(p, ws, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t indexer_scan(const dsa_indexer_args& a, float* scores, void* /*sel_ws*/, int32_t /*k*/,

@@ -76,9 +76,11 @@ def test_workspace_sizes_and_errors():
     assert need >= 8 * 204800 * 4
     assert topk_status(a, k=2048, ws=None, ws_bytes=0) == 3
     assert topk_status(a, k=2048, ws=FAKE, ws_bytes=need - 1) == 3
-    # prefill-shaped bf16 fused path needs no workspace
+    # prefill-shaped bf16 fused path: candidate slices for the persistent grid
     b = ix(n_q=16384, n_k=16384)
-    assert L.dsa_topk_workspace_size(ctypes.byref(b), None, 2048) == 0
+    fused = L.dsa_topk_workspace_size(ctypes.byref(b), None, 2048)
+    assert fused >= 512 * 4 * 2 * 16384 * 4
+    assert topk_status(b, k=2048, ws=FAKE, ws_bytes=fused - 1) == 3
     # materialised-scores path needs the select state
     assert L.dsa_topk_workspace_size(ctypes.byref(b), FAKE, 2048) > 0
     assert topk_status(b, k=2048, scores=FAKE) == 3
@@ -146,7 +148,7 @@ def test_forward_s_layers_need_no_indexer_inputs():
     """An S layer's indexer arguments are never read: validation (and workspace
     sizing) succeeds with every S-layer indexer pointer NULL."""
     arr = layers("FSSSFSSS", null_s=True)
-    assert L.indexcache_forward_workspace_size(b"FSSSFSSS", 8, arr, 16) == 0
+    assert L.indexcache_forward_workspace_size(b"FSSSFSSS", 8, arr, 16) > 0
     # the same NULL indexer on an F layer is rejected
     arr[0].ix = L.IndexerArgs()
     assert fwd_status("FSSSFSSS", arr) == 1

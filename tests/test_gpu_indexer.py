@@ -193,3 +193,39 @@ def test_determinism(dsa, dev):
     a = run_topk(dsa, ixi, 2048)
     b = run_topk(dsa, ixi, 2048)
     assert torch.equal(a, b)
+
+
+# --------------------------------------------------------------------------- long rows
+@pytest.mark.parametrize("dtype", [syn.BF16, syn.FP8])
+def test_fused_prefill_compaction_integer_exact(dsa, dev, dtype):
+    """Rows longer than the 16384-entry candidate buffer force compactions.  With
+    integer scores ties are massive, so the 16-bit-prefix shrink cannot free
+    space and the exact select (ties to the lower position) takes over."""
+    L = 40000
+    ixi = syn.indexer_inputs(B=1, n_q=L, dtype=dtype, values="int", w_dist="pow2", seed=31, device=dev)
+    rows = np.array([0, 2047, 16383, 16384, 16400, 20000, 33333, L - 2, L - 1])
+    check_exact(dsa, ixi, 2048, rows=rows)
+
+
+def test_fused_prefill_compaction_float(dsa, dev):
+    L = 40000
+    ixi = syn.indexer_inputs(B=1, n_q=L, dtype=syn.BF16, values="normal", w_dist="u8", seed=32, device=dev)
+    check_float(dsa, ixi, 2048, np.array([16383, 16384, 25000, L - 1]))
+
+
+@pytest.mark.parametrize("cid", [2, 3])
+def test_full_size_configs_sampled(dsa, dev, cid):
+    """Configs 2 (bf16, L=16384) and 3 (fp8, L=65536) at full size, in the launch
+    configuration the benchmark uses; sampled rows against the oracle."""
+    c = syn.CONFIGS[cid]
+    ixi = syn.indexer_inputs(B=1, n_q=c["L"], dtype=c["dtype"], values="normal", w_dist="u8", seed=c["seed"],
+                             device=dev)
+    rows = np.array([0, 2046, 2047, 2048, c["L"] // 2, c["L"] - 1])
+    check_float(dsa, ixi, c["topk"], rows)
+
+
+def test_full_size_config4_layer_integer_exact(dsa, dev):
+    """One F layer of the 8-layer L=131072 stack, integer-valued variant."""
+    layers = syn.c4_stack(L=131072, n_layers=1, seed=4, device=dev, values="int", with_sa=False)
+    ixi = layers[0][0]
+    check_exact(dsa, ixi, 2048, rows=np.array([5, 4095, 65536, 131070, 131071]))
