@@ -22,10 +22,18 @@ FLAGS = [
 ]
 
 
+# Per-file extra flags.  The indexer's inputs and MFMA results are finite: with
+# NaNs ruled out, fmaxf(x, 0) (the ReLU) is one v_max_f32 instead of a
+# NaN-quieting v_max plus the max.
+# MFMA results stay in VGPRs (the VALU epilogue reads them directly instead of
+# copying them out of AGPRs).
+EXTRA = {"indexer.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "packed-fp32-ops"
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l and l.strip())

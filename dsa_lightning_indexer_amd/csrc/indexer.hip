@@ -163,6 +163,21 @@ __device__ __forceinline__ void load_row(const IxParams& p, int64_t gi, int lane
   }
 }
 
+// Consume the row's q fragments and weights in an empty asm statement so their
+// loads are waited for once here; otherwise the wait-count pass treats them as
+// possibly in flight on every iteration of the tile loop and drains the tile
+// prefetch along with them.
+template <int DT, int D, int HT>
+__device__ __forceinline__ void settle_row(RowState<DT, D, HT>& rs) {
+#pragma unroll
+  for (int h = 0; h < HT; ++h) {
+#pragma unroll
+    for (int ks = 0; ks < Cfg<DT, D>::NKS; ++ks) asm volatile("" : "+v"(rs.a[h][ks]));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(rs.c[h][i]));
+  }
+}
+
 // Scores of keys [s0, s0+64) for the wave's row; lane l gets key s0 + l.
 // kt: LDS tile (PITCH-byte rows) or, when kt_global, the k row of key s0.
 template <int DT, int D, int HT>
@@ -178,11 +193,15 @@ __device__ __forceinline__ float tile_scores(const RowState<DT, D, HT>& rs, cons
 #pragma unroll
     for (int h = 0; h < HT; ++h) acc[h] = f32x16{};
     const uint8_t* rowp = kt + (32 * n + (lane & 31)) * pitch;
+    // B fragments are read one K step ahead of the MFMAs that consume them.
+    typename AFrag<DT>::T bf = load_frag<DT>(rowp, 0, lane);
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) {
-      typename AFrag<DT>::T bf = load_frag<DT>(rowp, ks, lane);
+      typename AFrag<DT>::T nxt = bf;
+      if (ks + 1 < C::NKS) nxt = load_frag<DT>(rowp, ks + 1, lane);
 #pragma unroll
       for (int h = 0; h < HT; ++h) acc[h] = mfma<DT>(rs.a[h][ks], bf, acc[h]);
+      bf = nxt;
     }
     // 32x32 output: lane l holds column (key) l%32 and rows 8*(i/4) + 4*(l/32) + i%4.
     float pp = 0.f;
@@ -195,10 +214,12 @@ __device__ __forceinline__ float tile_scores(const RowState<DT, D, HT>& rs, cons
   }
   // lanes l and l^32 hold complementary head rows of the same key column:
   // lanes 0-31 finish keys 0-31 (subtile 0), lanes 32-63 keys 32-63 (subtile 1).
-  const bool lo = lane < 32;
-  const float send = lo ? part[1] : part[0];
-  const float recv = __shfl_xor(send, 32, 64);
-  return (lo ? part[0] : part[1]) + recv;
+  // v_permlane32_swap(x = part[0], y = part[1]) exchanges the upper half of x
+  // with the lower half of y: afterwards x holds subtile 0's partials of lanes
+  // 0-31 in both halves, y subtile 1's partials of lanes 32-63 in both halves.
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]),
+                                                   false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
 // Cooperative 256-thread copy of the 64-key tile `tile` into registers, then LDS
@@ -225,6 +246,39 @@ __device__ __forceinline__ void store_ktile(uint8_t* dst, const i32x4 (&pre)[Cfg
     *(i32x4*)(&dst[key * C::PITCH + part * 16]) = pre[j];
   }
 }
+
+// Buffer-resource view of a byte range (gfx9 family resource word: raw buffer,
+// out-of-range reads return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Per-thread, loop-invariant offsets of the tile copy: chunk j of thread tid is
+// 16-byte part (c % CPR) of key (c / CPR), c = tid + 256 j.
+template <int DT, int D>
+struct TileCopy {
+  typedef Cfg<DT, D> C;
+  uint32_t goff[C::NCH];   // byte offset inside a tile of k rows in HBM
+  uint32_t loff[C::NCH];   // byte offset inside an LDS tile
+  __device__ __forceinline__ TileCopy() {
+#pragma unroll
+    for (int j = 0; j < C::NCH; ++j) {
+      const int c = threadIdx.x + 256 * j;
+      goff[j] = (uint32_t)((c / C::CPR) * C::ROWB + (c % C::CPR) * 16);
+      loff[j] = (uint32_t)((c / C::CPR) * C::PITCH + (c % C::CPR) * 16);
+    }
+  }
+  // keys at or past the buffer's end read as zero
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int tile, i32x4 (&pre)[C::NCH]) const {
+    const int soff = tile * kTileKeys * C::ROWB;
+#pragma unroll
+    for (int j = 0; j < C::NCH; ++j) pre[j] = __builtin_amdgcn_raw_buffer_load_b128(r, goff[j], soff, 0);
+  }
+  __device__ __forceinline__ void store(uint8_t* dst, const i32x4 (&pre)[C::NCH]) const {
+#pragma unroll
+    for (int j = 0; j < C::NCH; ++j) *(i32x4*)(dst + loff[j]) = pre[j];
+  }
+};
 
 // ---------------------------------------------------------------- wave select
 // A wave owns one query row's candidate buffer (order keys cu[], positions ci[])
@@ -413,9 +467,13 @@ __global__ __launch_bounds__(256, 2) void ix_topk_kernel(IxParams p, uint32_t* w
   const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
   uint32_t* cu = cand + ((size_t)blockIdx.x * kRowsPerBlock + wid) * 2 * kCandCap;
   uint32_t* ci = cu + kCandCap;
+  // candidate slice as a buffer: appends are 32-bit offsets (keys at [0, cap),
+  // positions at [cap, 2 cap))
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(cu, 2u * kCandCap * 4u);
   const int64_t nrb = (p.rows + kRowsPerBlock - 1) / kRowsPerBlock;
   const int64_t total = nrb * p.batch;
   const int k = p.topk;
+  const TileCopy<DT, D> tc;
 
   for (;;) {
     if (threadIdx.x == 0) s_item = (int64_t)atomicAdd(work, 1u);
@@ -429,56 +487,61 @@ __global__ __launch_bounds__(256, 2) void ix_topk_kernel(IxParams p, uint32_t* w
     const int64_t rloc = rloc0 + wid;
     const bool vrow = rloc < p.rows;
     const int64_t i = p.row0 + rloc;
-    const int64_t t = p.q_pos0 + i;
+    // positions fit in 32 bits (n_k < 2^31)
+    const int t = vrow ? (int)(p.q_pos0 + i) : -1;
     const int64_t rlast = rloc0 + kRowsPerBlock - 1 < p.rows ? rloc0 + kRowsPerBlock - 1 : p.rows - 1;
     const int64_t t_last = p.q_pos0 + p.row0 + rlast;
-    const int64_t nkeys = t_last + 1 < p.n_k ? t_last + 1 : p.n_k;
-    const int ntiles = (int)((nkeys + kTileKeys - 1) / kTileKeys);
+    const int nkeys = (int)(t_last + 1 < p.n_k ? t_last + 1 : p.n_k);
+    const int ntiles = (nkeys + kTileKeys - 1) / kTileKeys;
+    const int tlim = t < p.n_k - 1 ? t : p.n_k - 1;             // last candidate position
     const int64_t gi = (int64_t)b * p.n_q + i;
 
     RowState<DT, D, HT> rs;
     if (vrow) load_row<DT, D, HT>(p, gi, lane, rs);
+    settle_row(rs);
     const uint8_t* kbase = (const uint8_t*)p.k + (int64_t)b * p.k_bs * C::ES;
-    const float* ksc = (DT == DT_FP8) ? p.k_scale + (int64_t)b * p.ks_bs : nullptr;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (uint32_t)nkeys * C::ROWB);
+    // fp8 key scales (unused for bf16: an empty range)
+    const __amdgpu_buffer_rsrc_t srs =
+        make_rsrc(DT == DT_FP8 ? (const void*)(p.k_scale + (int64_t)b * p.ks_bs) : (const void*)kbase,
+                  DT == DT_FP8 ? (uint32_t)nkeys * 4u : 0u);
 
     int cnt = 0;
     bool full = false, strict = false;
     uint32_t thr = 0;
     i32x4 pre[C::NCH];
     if (ntiles > 0) {
-      load_ktile<DT, D>(kbase, p.n_k, 0, pre);
-      store_ktile<DT, D>(ktile[0], pre);
+      tc.load(krs, 0, pre);
+      tc.store(ktile[0], pre);
     }
     for (int it = 0; it < ntiles; ++it) {
       __syncthreads();
-      if (it + 1 < ntiles) load_ktile<DT, D>(kbase, p.n_k, it + 1, pre);
-      const int64_t s0 = (int64_t)it * kTileKeys;
-      if (vrow && s0 <= t) {
+      if (it + 1 < ntiles) tc.load(krs, it + 1, pre);
+      const int s0 = it * kTileKeys;
+      if (s0 <= tlim) {
         float sc = tile_scores<DT, D, HT>(rs, &ktile[it & 1][0], C::PITCH, lane);
-        const int64_t s = s0 + lane;
-        if constexpr (DT == DT_FP8) {
-          if (s < p.n_k) sc *= ksc[s];
-        }
-        const bool valid = s <= t && s < p.n_k;
+        const int s = s0 + lane;
+        if constexpr (DT == DT_FP8) sc *= __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, lane * 4, s0 * 4, 0));
         const uint32_t u = order_key(sc);
         if (cnt + 64 > kCandCap) {
-          lds_sync();
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
           cnt = wave_shrink(cu, ci, cnt, k, hist[wid], lane, thr, strict);
           full = true;
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
         }
-        const bool pr = valid && (!full || (strict ? u > thr : u >= thr));
+        const bool pr = s <= tlim && (!full || (strict ? u > thr : u >= thr));
         const uint64_t m = ballot(pr);
         if (pr) {
-          const int d = cnt + (int)lanes_below(m);
-          cu[d] = u;
-          ci[d] = (uint32_t)s;
+          const uint32_t d = (uint32_t)cnt + lanes_below(m);
+          __builtin_amdgcn_raw_buffer_store_b32(u, crs, d * 4u, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32((uint32_t)s, crs, d * 4u, kCandCap * 4, 0);
         }
         cnt += __builtin_popcountll(m);
       }
-      if (it + 1 < ntiles) store_ktile<DT, D>(ktile[(it + 1) & 1], pre);
+      if (it + 1 < ntiles) tc.store(ktile[(it + 1) & 1], pre);
     }
     if (vrow) {
-      lds_sync();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
       int32_t* out = p.idx + gi * (int64_t)k;
       int nout;
       if (cnt > k) {
