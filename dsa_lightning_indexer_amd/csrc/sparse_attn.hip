@@ -112,18 +112,33 @@ __global__ __launch_bounds__(256) void sa_generic_kernel(SAParams p) {
 
 // ---------------------------------------------------------------- MLA MFMA path
 constexpr int kH = 16;       // query heads per latent row
-constexpr int kTile = 16;    // selected positions per wave step
+constexpr int kTile = 16;    // selected positions per step
 
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// One wave per (query row, split of its index row).  Per 16-position step:
+//   1. the 16 gathered latent rows arrive in registers as the A operand of
+//      S^T = K_sel . Q^T (16x16x32 bf16 MFMA, lane = position l%16, 8 columns);
+//      the next step's rows are already being fetched (register double buffer);
+//   2. their first DV columns are stored to a row-major LDS tile (16-byte
+//      writes) and read back transposed with ds_read_b64_tr_b16, which hands
+//      every lane V[4g..4g+3][d0 + l%16] -- the V^T A operand of the 16x16x16
+//      MFMA -- when lane s of lane group g points at V[4g + s/4][d0 + 4(s%4)];
+//   3. online softmax per head: the S^T accumulator puts one head per lane and
+//      4 consecutive positions in its registers, which is already the P^T B
+//      operand; P is split into bf16 hi + lo so P.V keeps ~2^-17 relative
+//      accuracy of the weights;
+//   4. O^T[DV x 16] += V^T . P^T; rescaling of O is skipped when no head's
+//      running max moved.
 template <int DQK, int DV>
-__global__ __launch_bounds__(256, 1) void sa_mla_kernel(SAParams p) {
+__global__ __launch_bounds__(64) void sa_mla_kernel(SAParams p) {
   constexpr int NKS = DQK / 32;        // 16x16x32 K steps for Q.K
-  constexpr int NVS = DV / 32;         // of those, the ones that carry V columns
+  constexpr int NVS = DV / 32;         // K steps whose 8-column slices are V columns
   constexpr int NDT = DV / 16;         // output tiles of 16 V columns
-  __shared__ __attribute__((aligned(16))) __bf16 vt[4][DV][kTile];   // V^T per wave
-  __shared__ float obuf[kH][DV];
-  __shared__ float sm[4][kH], sl[4][kH];
+  constexpr int PITCH = DV * 2 + 32;   // LDS row pitch in bytes (bank spread)
+  __shared__ __attribute__((aligned(16))) uint8_t vt[kTile * PITCH];
 
-  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lane = threadIdx.x;
   const int g = lane >> 4, col = lane & 15;
   const int split = (int)(blockIdx.x % p.nsplit);
   const int64_t gi = blockIdx.x / p.nsplit;          // flattened (batch, query row)
@@ -132,7 +147,7 @@ __global__ __launch_bounds__(256, 1) void sa_mla_kernel(SAParams p) {
   const int e0 = split * per;
   const int e1 = e0 + per < p.topk ? e0 + per : p.topk;
 
-  // Q^T as the B operand: lane holds head `col`, dims 32*ks + 8*g .. +8.
+  // Q^T as the B operand: lane holds head `col`, columns 32*ks + 8*g .. +8.
   bf16x8 qf[NKS];
   const __bf16* qrow = (const __bf16*)p.q + (gi * kH + col) * (int64_t)DQK;
 #pragma unroll
@@ -145,44 +160,42 @@ __global__ __launch_bounds__(256, 1) void sa_mla_kernel(SAParams p) {
 
   const __bf16* kvb = (const __bf16*)p.kv + (int64_t)b * p.kv_bs;
   const int32_t* ir = p.idx + gi * (int64_t)p.topk;
+  // this lane's write slot and transposed-read address inside the LDS tile
+  uint8_t* wrow = vt + col * PITCH + 16 * g;
+  const uint8_t* rbase = vt + (4 * g + (col >> 2)) * PITCH + 8 * (col & 3);
 
-  for (int tb = e0 + kTile * wid; tb < e1; tb += 4 * kTile) {
+  // Gather the 16 latent rows of the step starting at entry tb into kb (zeros for
+  // invalid entries); vm gets the valid-position mask.
+  auto fetch = [&](int tb, bf16x8 (&kb)[NKS], uint64_t& vm) {
     const int e = tb + col;
-    int32_t s = e < e1 ? ir[e] : -1;
+    const int32_t s = e < e1 ? ir[e] : -1;
     const bool valid = s >= 0 && s < p.n_k;
-    const uint64_t vm = ballot(valid);
+    vm = ballot(valid);
     const __bf16* rowp = kvb + (int64_t)(valid ? s : 0) * DQK;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) kb[ks] = valid ? *(const bf16x8*)(rowp + 32 * ks + 8 * g) : bf16x8{};
+  };
+  auto step = [&](const bf16x8 (&kb)[NKS], uint64_t vm) {
     f32x4 acc = f32x4{};
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      bf16x8 a = valid ? *(const bf16x8*)(rowp + 32 * ks + 8 * g) : bf16x8{};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], acc, 0, 0, 0);
-      if (ks < NVS) {
+    for (int ks = 0; ks < NKS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[ks], qf[ks], acc, 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) vt[wid][32 * ks + 8 * g + j][col] = a[j];
-      }
-    }
-    // acc[i]: head `col`, key 4*g + i of this tile.
+    for (int ks = 0; ks < NVS; ++ks) *(bf16x8*)(wrow + 64 * ks) = kb[ks];
+    // acc[i]: head `col`, position 4*g + i of this step.
     float z[4];
     float mx = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool kv_ok = (vm >> (4 * g + i)) & 1ull;
-      z[i] = kv_ok ? acc[i] * p.scale : -__builtin_inff();
+      z[i] = ((vm >> (4 * g + i)) & 1ull) ? acc[i] * p.scale : -__builtin_inff();
       mx = fmaxf(mx, z[i]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx);
-    // P is split into bf16 hi + lo parts (P ~= hi + lo to ~2^-17 relative) so the
-    // bf16 MFMA P.V keeps fp32-level accuracy of the softmax weights.
-    bf16x4 pb_hi, pb_lo;
+    bf16x4 pb_hi = bf16x4{}, pb_lo = bf16x4{};
     float alpha = 1.f;
-    if (m_new == -__builtin_inff()) {
-      pb_hi = bf16x4{};
-      pb_lo = bf16x4{};
-    } else {
-      alpha = (m_run == -__builtin_inff()) ? 0.f : __expf(m_run - m_new);
+    if (m_new != -__builtin_inff()) {
+      alpha = (m_run == m_new) ? 1.f : ((m_run == -__builtin_inff()) ? 0.f : __expf(m_run - m_new));
       float ps = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -195,62 +208,48 @@ __global__ __launch_bounds__(256, 1) void sa_mla_kernel(SAParams p) {
       l_run = l_run * alpha + ps;
       m_run = m_new;
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    if (ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      o[dt] *= alpha;
-      const bf16x4 va = *(const bf16x4*)&vt[wid][16 * dt + col][4 * g];
+      const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(rbase + 32 * dt));
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_hi, o[dt], 0, 0, 0);
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_lo, o[dt], 0, 0, 0);
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  };
+
+  // two register buffers, alternated by unrolling the loop by two steps
+  bf16x8 kbA[NKS], kbB[NKS];
+  uint64_t vmA = 0, vmB = 0;
+  if (e0 < e1) fetch(e0, kbA, vmA);
+  for (int tb = e0; tb < e1; tb += 2 * kTile) {
+    if (tb + kTile < e1) fetch(tb + kTile, kbB, vmB);
+    step(kbA, vmA);
+    if (tb + kTile >= e1) break;
+    if (tb + 2 * kTile < e1) fetch(tb + 2 * kTile, kbA, vmA);
+    step(kbB, vmB);
   }
-  // Merge the four waves.
+  // row sum of head `col` = the sum over the 4 lanes holding it
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  if (g == 0) { sm[wid][col] = m_run; sl[wid][col] = l_run; }
-  __syncthreads();
-  float M = -__builtin_inff();
-#pragma unroll
-  for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][col]);
-  float L = 0.f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float mw = sm[w][col];
-    L += (mw == -__builtin_inff()) ? 0.f : sl[w][col] * __expf(mw - M);
-  }
-  const float myscale = (m_run == -__builtin_inff()) ? 0.f : __expf(m_run - M);
-  for (int w = 0; w < 4; ++w) {
-    if (wid == w) {
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = 16 * dt + 4 * g + i;
-          const float v = o[dt][i] * myscale;
-          obuf[col][d] = (w == 0) ? v : obuf[col][d] + v;
-        }
-      }
-    }
-    __syncthreads();
-  }
+  // O^T layout: lane holds head `col`, columns 16*dt + 4*g + (0..3)
   if (p.nsplit == 1) {
-    // every lane holding head `col` computed the same L; publish it once
-    if (wid == 0 && g == 0) sl[0][col] = L;
-    __syncthreads();
-    float* out = p.out + gi * (int64_t)kH * DV;
-    for (int x = threadIdx.x; x < kH * DV; x += 256) {
-      const int h = x / DV;
-      const float Lh = sl[0][h];
-      out[x] = Lh > 0.f ? obuf[h][x % DV] / Lh : 0.f;
-    }
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    float* out = p.out + (gi * kH + col) * (int64_t)DV + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) *(f32x4*)(out + 16 * dt) = o[dt] * inv;
   } else {
-    float* wo = p.ws_o + (gi * p.nsplit + split) * (int64_t)kH * DV;
-    for (int x = threadIdx.x; x < kH * DV; x += 256) wo[x] = obuf[x / DV][x % DV];
-    if (wid == 0 && g == 0) {
+    float* wo = p.ws_o + ((gi * p.nsplit + split) * kH + col) * (int64_t)DV + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) *(f32x4*)(wo + 16 * dt) = o[dt];
+    if (g == 0) {
       float* ml = p.ws_ml + ((gi * p.nsplit + split) * kH + col) * 2;
-      ml[0] = M;
-      ml[1] = L;
+      ml[0] = m_run;
+      ml[1] = l_run;
     }
   }
 }
@@ -285,7 +284,7 @@ bool mla_ok(const dsa_sparse_attn_args& a) {
 
 int pick_nsplit(const dsa_sparse_attn_args& a) {
   const int64_t rows = (int64_t)a.batch * a.n_q;
-  int64_t ns = (512 + rows - 1) / rows;
+  int64_t ns = (1024 + rows - 1) / rows;
   int64_t maxs = a.topk / 64;
   if (maxs < 1) maxs = 1;
   if (ns > maxs) ns = maxs;
@@ -327,7 +326,7 @@ hipError_t sparse_attn_launch(const dsa_sparse_attn_args& a, void* ws, hipStream
       p.ws_ml = p.ws_o + rows * p.nsplit * a.heads * (int64_t)a.d_v;
     }
     dim3 grid((unsigned)(rows * p.nsplit));
-    hipLaunchKernelGGL((sa_mla_kernel<576, 512>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((sa_mla_kernel<576, 512>), grid, dim3(64), 0, s, p);
     if (p.nsplit > 1) {
       hipLaunchKernelGGL(sa_combine_kernel, dim3((unsigned)(rows * a.heads)), dim3(256), 0, s, p);
     }
