@@ -222,16 +222,21 @@ __global__ __launch_bounds__(64) void sa_mla_kernel(SAParams p) {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   };
 
-  // two register buffers, alternated by unrolling the loop by two steps
-  bf16x8 kbA[NKS], kbB[NKS];
-  uint64_t vmA = 0, vmB = 0;
+  // three register buffers (two steps of gathers in flight while one computes),
+  // rotated by unrolling the loop by three steps
+  bf16x8 kbA[NKS], kbB[NKS], kbC[NKS];
+  uint64_t vmA = 0, vmB = 0, vmC = 0;
   if (e0 < e1) fetch(e0, kbA, vmA);
-  for (int tb = e0; tb < e1; tb += 2 * kTile) {
-    if (tb + kTile < e1) fetch(tb + kTile, kbB, vmB);
+  if (e0 + kTile < e1) fetch(e0 + kTile, kbB, vmB);
+  for (int tb = e0; tb < e1; tb += 3 * kTile) {
+    if (tb + 2 * kTile < e1) fetch(tb + 2 * kTile, kbC, vmC);
     step(kbA, vmA);
     if (tb + kTile >= e1) break;
-    if (tb + 2 * kTile < e1) fetch(tb + 2 * kTile, kbA, vmA);
+    if (tb + 3 * kTile < e1) fetch(tb + 3 * kTile, kbA, vmA);
     step(kbB, vmB);
+    if (tb + 2 * kTile >= e1) break;
+    if (tb + 4 * kTile < e1) fetch(tb + 4 * kTile, kbB, vmB);
+    step(kbC, vmC);
   }
   // row sum of head `col` = the sum over the 4 lanes holding it
   l_run += __shfl_xor(l_run, 16, 64);
@@ -254,25 +259,37 @@ __global__ __launch_bounds__(64) void sa_mla_kernel(SAParams p) {
   }
 }
 
+// Merge the split partials of one (query row, head): weights exp(m_s - M) are
+// computed once into LDS, then each thread accumulates its output columns.
 __global__ __launch_bounds__(256) void sa_combine_kernel(SAParams p) {
+  __shared__ float wsum[2];
+  __shared__ float wgt[128];
   const int h = blockIdx.x % p.heads;
   const int64_t gi = blockIdx.x / p.heads;
-  float M = -__builtin_inff();
-  for (int sp = 0; sp < p.nsplit; ++sp) M = fmaxf(M, p.ws_ml[((gi * p.nsplit + sp) * p.heads + h) * 2]);
-  float L = 0.f;
-  for (int sp = 0; sp < p.nsplit; ++sp) {
-    const float* ml = p.ws_ml + ((gi * p.nsplit + sp) * p.heads + h) * 2;
-    L += (ml[0] == -__builtin_inff()) ? 0.f : ml[1] * __expf(ml[0] - M);
+  const float* ml = p.ws_ml + (gi * p.nsplit * p.heads + h) * 2;   // split stride: heads * 2
+  if (threadIdx.x < 64) {
+    float m = -__builtin_inff();
+    for (int sp = threadIdx.x; sp < p.nsplit; sp += 64) m = fmaxf(m, ml[(int64_t)sp * p.heads * 2]);
+    const float M = wave_max(m);
+    float L = 0.f;
+    for (int sp = threadIdx.x; sp < p.nsplit; sp += 64) {
+      const float ms = ml[(int64_t)sp * p.heads * 2];
+      const float w = (ms == -__builtin_inff()) ? 0.f : __expf(ms - M);
+      wgt[sp] = w;
+      L += w * ml[(int64_t)sp * p.heads * 2 + 1];
+    }
+    L = wave_sum(L);
+    if (threadIdx.x == 0) wsum[0] = L > 0.f ? 1.f / L : 0.f;
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
+  __syncthreads();
+  const float inv = wsum[0];
+  const float* po = p.ws_o + (gi * p.nsplit * p.heads + h) * (int64_t)p.d_v;
+  const int64_t sstride = (int64_t)p.heads * p.d_v;
   float* out = p.out + (gi * p.heads + h) * (int64_t)p.d_v;
   for (int c = threadIdx.x; c < p.d_v; c += blockDim.x) {
     float acc = 0.f;
-    for (int sp = 0; sp < p.nsplit; ++sp) {
-      const float m = p.ws_ml[((gi * p.nsplit + sp) * p.heads + h) * 2];
-      if (m == -__builtin_inff()) continue;
-      acc += p.ws_o[((gi * p.nsplit + sp) * p.heads + h) * (int64_t)p.d_v + c] * __expf(m - M);
-    }
+#pragma unroll 8
+    for (int sp = 0; sp < p.nsplit; ++sp) acc = fmaf(wgt[sp], po[sp * sstride + c], acc);
     out[c] = acc * inv;
   }
 }
