@@ -112,6 +112,8 @@ dsa_status check_topk(const dsa_indexer_args* a, const float* scores, int32_t k,
     st = check_indexer_data(a);
     if (st != DSA_OK) return st;
   }
+  if (topk_path(a, scores) != PATH_FUSED && a->n_k > (int32_t)dsa_host::kSelectMaxRow)
+    return fail(DSA_ERR_UNSUPPORTED, "this Top-k path handles rows of at most %d scores", dsa_host::kSelectMaxRow);
   const size_t need = topk_ws(a, scores);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);

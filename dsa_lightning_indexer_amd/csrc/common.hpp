@@ -74,6 +74,7 @@ struct SelectPlan {
   int64_t row_stride;  // elements between score rows
 };
 
+constexpr int kSelectMaxRow = 1024 * 4096;   // longest score row the select handles
 size_t select_workspace_bytes(int64_t rows);
 // Zero the select state (fill kernel; safe under stream capture).
 hipError_t select_prepare(void* ws, int64_t rows, hipStream_t s);

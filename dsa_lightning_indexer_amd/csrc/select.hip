@@ -17,8 +17,9 @@
 
 namespace {
 
-constexpr int kRowWords = 8464;        // per-row workspace (u32)
-constexpr int kH1 = 0, kH2 = 4096, kH3 = 8192, kSt = 8448;
+constexpr int kMaxChunks = 1024;       // rows up to kMaxChunks * kChunk = 4M scores
+constexpr int kH1 = 0, kH2 = 4096, kH3 = 8192, kSt = 8448, kCnt = 8464;
+constexpr int kRowWords = kCnt + 2 * kMaxChunks;   // per-row workspace (u32)
 // state words
 constexpr int kPrefix = 0, kMask = 1, kRem = 2, kDone1 = 4, kDone2 = 5, kDone3 = 6;
 constexpr int kChunk = 4096;           // scores per histogram workgroup
@@ -120,9 +121,18 @@ __global__ __launch_bounds__(kHistThreads) void hist_kernel(const float* __restr
     const float* row = scores + r * row_stride;
     const int64_t b0 = (int64_t)blockIdx.y * kChunk;
     const int64_t b1 = b0 + kChunk < len ? b0 + kChunk : len;
-    for (int64_t s = b0 + threadIdx.x; s < b1; s += kHistThreads) {
-      uint32_t u = dsa::order_key(row[s]);
-      if ((u & mask) == prefix) atomicAdd(&h[(u >> SHIFT) & DMASK], 1u);
+    constexpr int PER = kChunk / kHistThreads;
+    float v[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int64_t s = b0 + threadIdx.x + (int64_t)j * kHistThreads;
+      v[j] = s < b1 ? row[s] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int64_t s = b0 + threadIdx.x + (int64_t)j * kHistThreads;
+      const uint32_t u = dsa::order_key(v[j]);
+      if (s < b1 && (u & mask) == prefix) atomicAdd(&h[(u >> SHIFT) & DMASK], 1u);
     }
     __syncthreads();
     for (int i = threadIdx.x; i < NB; i += kHistThreads) {
@@ -142,66 +152,121 @@ __global__ __launch_bounds__(kHistThreads) void hist_kernel(const float* __restr
   find_digit(rw + HOFF, NB, SHIFT, DMASK, rem, prefix, mask, st, sh);
 }
 
-constexpr int kWriteThreads = 1024;
+// Per chunk: how many entries beat T and how many tie with it.  Each thread
+// reads kPerThread consecutive entries (so chunk order = thread order).
+constexpr int kPerThread = kChunk / kHistThreads;
 
-// One workgroup per row: ordered write of the selected positions.
-__global__ __launch_bounds__(kWriteThreads) void write_kernel(const float* __restrict__ scores,
-                                                              int64_t row_stride, int32_t n_q,
-                                                              int64_t q_pos0, int32_t n_k,
-                                                              int32_t k, const uint32_t* ws,
-                                                              int32_t* __restrict__ idx) {
+__device__ __forceinline__ void load_run(const float* row, int64_t s0, int64_t len, float (&v)[kPerThread]) {
+  if (s0 + kPerThread <= len && (((uintptr_t)(row + s0)) & 15) == 0) {
+#pragma unroll
+    for (int j = 0; j < kPerThread; j += 4) {
+      const float4 q = *(const float4*)(row + s0 + j);
+      v[j] = q.x; v[j + 1] = q.y; v[j + 2] = q.z; v[j + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) v[j] = s0 + j < len ? row[s0 + j] : 0.f;
+  }
+}
+
+__global__ __launch_bounds__(kHistThreads) void count_kernel(const float* __restrict__ scores,
+                                                             int64_t row_stride, int32_t n_q,
+                                                             int64_t q_pos0, int32_t n_k, int32_t k,
+                                                             uint32_t* __restrict__ ws) {
   __shared__ uint32_t sh[17];
   const int64_t r = blockIdx.x;
-  const uint32_t* st = ws + r * kRowWords + kSt;
+  const int64_t len = row_len(r, n_q, q_pos0, n_k);
+  if (len <= k) return;                                   // take-all rows need no counts
+  uint32_t* rw = ws + r * kRowWords;
+  const uint32_t T = ld_agent(&rw[kSt + kPrefix]);
+  const int64_t s0 = (int64_t)blockIdx.y * kChunk + (int64_t)threadIdx.x * kPerThread;
+  float v[kPerThread];
+  load_run(scores + r * row_stride, s0, len, v);
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const uint32_t u = dsa::order_key(v[j]);
+    const bool in = s0 + j < len;
+    gt += (in && u > T) ? 1u : 0u;
+    eq += (in && u == T) ? 1u : 0u;
+  }
+  uint32_t tg, te;
+  block_excl_scan(gt, &tg, sh);
+  block_excl_scan(eq, &te, sh);
+  if (threadIdx.x == 0) {
+    rw[kCnt + 2 * blockIdx.y] = tg;
+    rw[kCnt + 2 * blockIdx.y + 1] = te;
+  }
+}
+
+// Ordered write: chunk p's kept entries start after those of chunks 0..p-1;
+// ties at T are kept in position order until the quota is used.
+__global__ __launch_bounds__(kHistThreads) void write_kernel(const float* __restrict__ scores,
+                                                             int64_t row_stride, int32_t n_q,
+                                                             int64_t q_pos0, int32_t n_k, int32_t k,
+                                                             const uint32_t* __restrict__ ws,
+                                                             int32_t* __restrict__ idx) {
+  __shared__ uint32_t sh[17];
+  const int64_t r = blockIdx.x;
+  const int p = blockIdx.y;
   const int64_t len = row_len(r, n_q, q_pos0, n_k);
   int32_t* out = idx + r * (int64_t)k;
-  const bool take_all = len <= k;
-  const uint32_t T = take_all ? 0u : ld_agent(&st[kPrefix]);
-  const uint32_t req = take_all ? 0u : ld_agent(&st[kRem]);
-  const float* row = scores + r * row_stride;
-  uint32_t base = 0, eq_base = 0;
-  constexpr int PER = 4;
-  for (int64_t t0 = 0; t0 < len; t0 += (int64_t)kWriteThreads * PER) {
-    const int64_t s0 = t0 + (int64_t)threadIdx.x * PER;
-    bool keep[PER];
-    uint32_t nk = 0, ne = 0;
-    uint32_t u[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int64_t s = s0 + j;
-      u[j] = s < len ? dsa::order_key(row[s]) : 0u;
-      ne += (s < len && !take_all && u[j] == T) ? 1u : 0u;
-    }
-    uint32_t ne_tot;
-    uint32_t eq_ex = block_excl_scan(ne, &ne_tot, sh) + eq_base;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int64_t s = s0 + j;
-      bool in = s < len;
-      bool kp;
-      if (take_all) {
-        kp = in;
-      } else {
-        bool tie = in && u[j] == T;
-        kp = in && (u[j] > T || (tie && eq_ex < req));
-        eq_ex += tie ? 1u : 0u;
-      }
-      keep[j] = kp;
-      nk += kp ? 1u : 0u;
-    }
-    uint32_t nk_tot;
-    uint32_t pos = block_excl_scan(nk, &nk_tot, sh) + base;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      if (keep[j]) {
-        if (pos < (uint32_t)k) out[pos] = (int32_t)(s0 + j);
-        ++pos;
-      }
-    }
-    base += nk_tot;
-    eq_base += ne_tot;
+  const int64_t kept_total = len < k ? len : (int64_t)k;
+  if (p == 0) {
+    for (int64_t j = kept_total + threadIdx.x; j < k; j += kHistThreads) out[j] = -1;
   }
-  for (int64_t j = base + threadIdx.x; j < k; j += kWriteThreads) out[j] = -1;
+  const int64_t c0 = (int64_t)p * kChunk;
+  if (c0 >= len) return;
+  const int64_t s0 = c0 + (int64_t)threadIdx.x * kPerThread;
+  if (len <= k) {                                        // take all: position s goes to slot s
+    for (int j = 0; j < kPerThread; ++j)
+      if (s0 + j < len) out[s0 + j] = (int32_t)(s0 + j);
+    return;
+  }
+  const uint32_t* rw = ws + r * kRowWords;
+  const uint32_t T = ld_agent(&rw[kSt + kPrefix]);
+  const uint32_t req = ld_agent(&rw[kSt + kRem]);
+  // Chunks before this one: sum of their counts.  Ties are kept in position
+  // order until the quota req is used, so they contribute min(req, their ties).
+  uint32_t gsum = 0, esum = 0;
+  for (int q = threadIdx.x; q < p; q += kHistThreads) {
+    gsum += ld_agent(&rw[kCnt + 2 * q]);
+    esum += ld_agent(&rw[kCnt + 2 * q + 1]);
+  }
+  uint32_t gtot, etot;
+  block_excl_scan(gsum, &gtot, sh);
+  block_excl_scan(esum, &etot, sh);
+  const uint32_t eq_before = etot;
+  const uint32_t base = gtot + (etot < req ? etot : req);
+  float v[kPerThread];
+  load_run(scores + r * row_stride, s0, len, v);
+  uint32_t u[kPerThread];
+  uint32_t ne = 0;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    u[j] = dsa::order_key(v[j]);
+    ne += (s0 + j < len && u[j] == T) ? 1u : 0u;
+  }
+  uint32_t tot;
+  uint32_t tie = block_excl_scan(ne, &tot, sh) + eq_before;
+  bool keep[kPerThread];
+  uint32_t nk = 0;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const bool in = s0 + j < len;
+    const bool t_ = in && u[j] == T;
+    keep[j] = in && (u[j] > T || (t_ && tie < req));
+    tie += t_ ? 1u : 0u;
+    nk += keep[j] ? 1u : 0u;
+  }
+  uint32_t pos = block_excl_scan(nk, &tot, sh) + base;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    if (keep[j]) {
+      if (pos < (uint32_t)k) out[pos] = (int32_t)(s0 + j);
+      ++pos;
+    }
+  }
 }
 
 inline int64_t max_len(const dsa_host::SelectPlan& p) {
@@ -240,8 +305,10 @@ hipError_t select_finish(const float* scores, const SelectPlan& p, void* ws, int
                      p.q_pos0, p.n_k, p.k, (uint32_t*)ws);
   hipLaunchKernelGGL(hist_kernel<3>, g, dim3(kHistThreads), 0, s, scores, p.row_stride, p.n_q,
                      p.q_pos0, p.n_k, p.k, (uint32_t*)ws);
-  hipLaunchKernelGGL(write_kernel, dim3((unsigned)p.rows), dim3(kWriteThreads), 0, s, scores,
-                     p.row_stride, p.n_q, p.q_pos0, p.n_k, p.k, (const uint32_t*)ws, idx);
+  hipLaunchKernelGGL(count_kernel, g, dim3(kHistThreads), 0, s, scores, p.row_stride, p.n_q,
+                     p.q_pos0, p.n_k, p.k, (uint32_t*)ws);
+  hipLaunchKernelGGL(write_kernel, g, dim3(kHistThreads), 0, s, scores, p.row_stride, p.n_q,
+                     p.q_pos0, p.n_k, p.k, (const uint32_t*)ws, idx);
   return hipGetLastError();
 }
 
