@@ -114,6 +114,9 @@ dsa_status check_topk(const dsa_indexer_args* a, const float* scores, int32_t k,
   }
   if (topk_path(a, scores) != PATH_FUSED && a->n_k > (int32_t)dsa_host::kSelectMaxRow)
     return fail(DSA_ERR_UNSUPPORTED, "this Top-k path handles rows of at most %d scores", dsa_host::kSelectMaxRow);
+  // the fused kernel addresses one batch's keys with 32-bit byte offsets
+  if (topk_path(a, scores) == PATH_FUSED && (int64_t)a->n_k * a->dim * (a->dtype == DSA_BF16 ? 2 : 1) >= (int64_t)1 << 31)
+    return fail(DSA_ERR_UNSUPPORTED, "fused indexer+Top-k needs n_k * dim * element size < 2^31 bytes");
   const size_t need = topk_ws(a, scores);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);

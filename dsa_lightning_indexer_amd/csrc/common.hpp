@@ -12,6 +12,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
@@ -27,6 +28,10 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }
+
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value:
+// derived from it, buffer resources and per-wave bases stay in SGPRs.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Lane-mask helpers (wave64).
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {

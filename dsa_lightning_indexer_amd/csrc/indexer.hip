@@ -89,6 +89,8 @@ struct Cfg {
   static constexpr int TILE_CHUNKS = kTileKeys * CPR;
   static constexpr int NCH = TILE_CHUNKS / 256;              // chunks per thread
   static constexpr int TILE_BYTES = kTileKeys * PITCH;
+  // staged tile of the fused kernel: the rows, then (fp8) the 64 key scales
+  static constexpr int BUF_BYTES = TILE_BYTES + (DT == DT_FP8 ? kTileKeys * 4 : 0);
 };
 
 template <int DT>
@@ -280,12 +282,94 @@ struct TileCopy {
   }
 };
 
+// One buffer_load ... lds of `bytes` (4 or 16) per lane at byte offset voff,
+// landing at LDS address lds + bytes * lane.  Issued from inline asm so that
+// the compiler's wait-count tracking, which would otherwise wait for the load
+// before every later LDS read of the same array, leaves it alone; callers wait
+// for it explicitly (vmcnt) before the barrier that publishes the data.  The
+// asm has no register outputs.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(__amdgpu_buffer_rsrc_t r, const uint8_t* lds, uint32_t voff) {
+  const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)lds;
+  if constexpr (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(a), "v"(voff), "s"(r) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(a), "v"(voff), "s"(r) : "memory", "m0");
+}
+
+// Workgroup barrier without the fence of __syncthreads (whose release would
+// wait for every load in flight, including the next tiles' staging): LDS
+// accesses before it have completed (lgkmcnt), the asm keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Direct HBM -> LDS staging of 64-key tiles (buffer_load ... lds).  Lane l of
+// one such load writes LDS bytes [base + 16 l, base + 16 l + 16), so a tile of
+// PITCH-byte rows (ROWB data bytes + 16 pad bytes) is SPR = CPR + 1 loads of 64
+// 16-byte slots: slot q holds part q % SPR of row q / SPR, and pad slots read
+// past the buffer's end (zeros).  Load j of a tile is issued by wave j % 4.
+// Offsets go in the per-lane offset so that the buffer's range check covers
+// them: keys at or past the end of the range read as zero.
+template <int DT, int D>
+struct TileDma {
+  typedef Cfg<DT, D> C;
+  static constexpr int SPR = C::CPR + 1;
+  static constexpr int NI = SPR + (DT == DT_FP8 ? 1 : 0);   // + one 4-byte-per-lane load of the key scales
+  static constexpr int NPW = (NI + 3) / 4;           // loads per wave and tile, at most
+  uint32_t goff[NPW];
+  int nload;                                          // loads this wave issues per tile
+  int wid;
+  __device__ __forceinline__ TileDma(int wid_, int lane) : wid(wid_) {
+    nload = (NI - wid_ + 3) / 4;
+#pragma unroll
+    for (int m = 0; m < NPW; ++m) {
+      const int q = 64 * (wid_ + 4 * m) + lane;
+      const int row = q / SPR, part = q % SPR;
+      goff[m] = part < C::CPR ? (uint32_t)(row * C::ROWB + part * 16) : 0x80000000u;
+    }
+  }
+  // sr: the key scales (fp8), as a buffer of floats
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, __amdgpu_buffer_rsrc_t sr, int tile,
+                                       uint8_t* dst, int lane) const {
+    const uint32_t toff = (uint32_t)tile * (kTileKeys * C::ROWB);
+#pragma unroll
+    for (int m = 0; m < NPW; ++m) {
+      const int j = wid + 4 * m;
+      if (j < SPR) {
+        lds_dma<16>(r, dst + j * 1024, goff[m] + toff);
+      } else if (DT == DT_FP8 && j == SPR) {
+        lds_dma<4>(sr, dst + C::TILE_BYTES, (uint32_t)(tile * kTileKeys + lane) * 4u);
+      }
+    }
+  }
+  // Wait until this wave's loads of the older of two tiles in flight are done
+  // (loads complete in issue order; the wave issues NPW or NPW-1 per tile).
+  __device__ __forceinline__ void wait_older() const {
+    // s_waitcnt encoding (gfx9): vmcnt in bits 3:0 (NPW <= 5 here); expcnt and lgkmcnt at their maxima
+    static_assert(NPW >= 1 && NPW <= 15, "vmcnt field");
+    if (nload == NPW) __builtin_amdgcn_s_waitcnt(0x0F70 | NPW);
+    else __builtin_amdgcn_s_waitcnt(0x0F70 | (NPW - 1));
+  }
+  __device__ __forceinline__ void wait_all() const { __builtin_amdgcn_s_waitcnt(0x0F70); }
+};
+
 // ---------------------------------------------------------------- wave select
 // A wave owns one query row's candidate buffer (order keys cu[], positions ci[])
 // in a private slice of the workspace.  Entries are appended in position order.
 __device__ __forceinline__ void lds_sync() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup"); }
 
 constexpr int kCandCap = 16384;        // candidates per row before a compaction
+
+// Entries [j, j+4) of a candidate array in one 16-byte load.  The arrays are
+// 16-byte aligned and their capacity is a multiple of 4, so a load that starts
+// below n stays inside the slice (entries at or past n are ignored).
+__device__ __forceinline__ u32x4 ld4(const uint32_t* p, int j) { return *(const u32x4*)(p + j); }
+
+// The select passes stream the candidate buffer from L2 with kSelVec 16-byte
+// loads in flight per lane (1024-2048 entries per wave step).
+constexpr int kSelVec = 8;
 
 // One radix pass: histogram of the 8-bit digit at `shift` among entries whose
 // masked key equals `prefix`; then pick the digit holding the rem-th largest.
@@ -296,17 +380,37 @@ __device__ uint32_t wave_radix_pass(const uint32_t* cu, int n, uint32_t prefix, 
 #pragma unroll
   for (int j = 0; j < 4; ++j) hist[lane * 4 + j] = 0u;
   lds_sync();
-  for (int j0 = 0; j0 < n; j0 += 64 * 8) {
-    uint32_t u[8];
+  for (int j0 = 0; j0 < n; j0 += 64 * 4 * kSelVec) {
+    u32x4 u[kSelVec];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int j = j0 + r * 64 + lane;
-      u[r] = j < n ? cu[j] : 0u;
+    for (int r = 0; r < kSelVec; ++r) {
+      const int j = j0 + 4 * (r * 64 + lane);
+      u[r] = j < n ? ld4(cu, j) : u32x4{};
     }
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int j = j0 + r * 64 + lane;
-      if (j < n && (u[r] & mask) == prefix) atomicAdd(&hist[(u[r] >> shift) & 255u], 1u);
+    for (int r = 0; r < kSelVec; ++r) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = j0 + 4 * (r * 64 + lane) + e;
+        const bool in = j < n && (u[r][e] & mask) == prefix;
+        const uint32_t d = (u[r][e] >> shift) & 255u;
+        if (shift != 24) {
+          if (in) atomicAdd(&hist[d], 1u);
+          continue;
+        }
+        // Top byte (sign and high exponent bits): nearly all keys share one
+        // digit, so the first active lane's digit is counted with a single
+        // add and only the other lanes use atomics (same-address LDS atomics
+        // serialise).
+        const uint64_t act = ballot(in);
+        if (act) {
+          const int lead = (int)__builtin_ctzll(act);
+          const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)d, lead);
+          const uint64_t same = ballot(in && d == d0);
+          if (lane == lead) atomicAdd(&hist[d0], (uint32_t)__builtin_popcountll(same));
+          else if (in && d != d0) atomicAdd(&hist[d], 1u);
+        }
+      }
     }
   }
   lds_sync();
@@ -338,38 +442,60 @@ __device__ uint32_t wave_radix_pass(const uint32_t* cu, int n, uint32_t prefix, 
 // (when tie_limit >= 0) the first tie_limit entries with key == T, or (when
 // tie_limit < 0) every entry with key == T.  With out_idx set, the kept
 // positions go there instead (at most `limit`).  Returns the number kept.
+// Each lane takes 4 consecutive entries per block; ranks in buffer order come
+// from one ballot per entry slot.  A step loads all its blocks before it
+// writes, and an entry is never written past its own slot, so in place is safe.
 __device__ int wave_keep(uint32_t* cu, uint32_t* ci, int n, uint32_t T, int64_t tie_limit, int lane,
                          int32_t* out_idx, int limit) {
+  constexpr int R = kSelVec;
   int out = 0;
   int64_t eqseen = 0;
-  for (int j0 = 0; j0 < n; j0 += 64 * 4) {
-    uint32_t u[4], id[4];
+  for (int j0 = 0; j0 < n; j0 += 64 * 4 * R) {
+    u32x4 u[R], id[R];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = j0 + r * 64 + lane;
-      u[r] = j < n ? cu[j] : 0u;
-      id[r] = j < n ? ci[j] : 0u;
+    for (int r = 0; r < R; ++r) {
+      const int j = j0 + 4 * (r * 64 + lane);
+      u[r] = j < n ? ld4(cu, j) : u32x4{};
+      id[r] = j < n ? ld4(ci, j) : u32x4{};
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = j0 + r * 64 + lane;
-      const bool in = j < n;
-      const bool tie = in && u[r] == T;
-      const uint64_t tm = ballot(tie);
-      const int64_t trank = eqseen + lanes_below(tm);
-      const bool keep = in && (u[r] > T || (tie && (tie_limit < 0 || trank < tie_limit)));
-      eqseen += __builtin_popcountll(tm);
-      const uint64_t km = ballot(keep);
-      if (keep) {
-        const int d = out + (int)lanes_below(km);
-        if (out_idx) {
-          if (d < limit) out_idx[d] = (int32_t)id[r];
-        } else if (d < limit) {
-          cu[d] = u[r];
-          ci[d] = id[r];
-        }
+    for (int r = 0; r < R; ++r) {
+      const int jb = j0 + 4 * (r * 64 + lane);
+      bool tie[4], keep[4];
+      uint64_t tm[4], km[4];
+      uint32_t tb = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        tie[e] = jb + e < n && u[r][e] == T;
+        tm[e] = ballot(tie[e]);
+        tb += lanes_below(tm[e]);
       }
-      out += __builtin_popcountll(km);
+      int64_t trank = eqseen + tb;
+      uint32_t kb = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        keep[e] = jb + e < n && (u[r][e] > T || (tie[e] && (tie_limit < 0 || trank < tie_limit)));
+        trank += tie[e] ? 1 : 0;
+        km[e] = ballot(keep[e]);
+        kb += lanes_below(km[e]);
+      }
+      int d = out + (int)kb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (keep[e]) {
+          if (d < limit) {
+            if (out_idx) {
+              out_idx[d] = (int32_t)id[r][e];
+            } else {
+              cu[d] = u[r][e];
+              ci[d] = id[r][e];
+            }
+          }
+          ++d;
+        }
+        eqseen += __builtin_popcountll(tm[e]);
+        out += __builtin_popcountll(km[e]);
+      }
     }
   }
   lds_sync();
@@ -423,7 +549,7 @@ template <int DT, int D, int HT>
 __global__ __launch_bounds__(256, 2) void ix_scores_kernel(IxParams p) {
   typedef Cfg<DT, D> C;
   __shared__ __attribute__((aligned(16))) uint8_t ktile[2][C::TILE_BYTES];
-  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wid = wave_id(), lane = threadIdx.x & 63;
   const int b = (int)(blockIdx.x % p.batch);
   const int64_t rloc = (int64_t)(blockIdx.x / p.batch) * kRowsPerBlock + wid;
   const bool vrow = rloc < p.rows;
@@ -460,11 +586,12 @@ __global__ __launch_bounds__(256, 2) void ix_scores_kernel(IxParams p) {
 template <int DT, int D, int HT>
 __global__ __launch_bounds__(256, 2) void ix_topk_kernel(IxParams p, uint32_t* work, uint32_t* cand) {
   typedef Cfg<DT, D> C;
-  __shared__ __attribute__((aligned(16))) uint8_t ktile[2][C::TILE_BYTES];
+  // three staging buffers: tiles it+1 and it+2 load while tile it is scored
+  __shared__ __attribute__((aligned(16))) uint8_t ktile[3][C::BUF_BYTES];
   __shared__ uint32_t hist[kRowsPerBlock][256];
   __shared__ int64_t s_item;
 
-  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wid = wave_id(), lane = threadIdx.x & 63;
   uint32_t* cu = cand + ((size_t)blockIdx.x * kRowsPerBlock + wid) * 2 * kCandCap;
   uint32_t* ci = cu + kCandCap;
   // candidate slice as a buffer: appends are 32-bit offsets (keys at [0, cap),
@@ -473,7 +600,7 @@ __global__ __launch_bounds__(256, 2) void ix_topk_kernel(IxParams p, uint32_t* w
   const int64_t nrb = (p.rows + kRowsPerBlock - 1) / kRowsPerBlock;
   const int64_t total = nrb * p.batch;
   const int k = p.topk;
-  const TileCopy<DT, D> tc;
+  const TileDma<DT, D> td(wid, lane);
 
   for (;;) {
     if (threadIdx.x == 0) s_item = (int64_t)atomicAdd(work, 1u);
@@ -509,19 +636,20 @@ __global__ __launch_bounds__(256, 2) void ix_topk_kernel(IxParams p, uint32_t* w
     int cnt = 0;
     bool full = false, strict = false;
     uint32_t thr = 0;
-    i32x4 pre[C::NCH];
-    if (ntiles > 0) {
-      tc.load(krs, 0, pre);
-      tc.store(ktile[0], pre);
-    }
+    td.load(krs, srs, 0, ktile[0], lane);
+    if (ntiles > 1) td.load(krs, srs, 1, ktile[1], lane);
     for (int it = 0; it < ntiles; ++it) {
-      __syncthreads();
-      if (it + 1 < ntiles) tc.load(krs, it + 1, pre);
+      // this wave's loads of tile it are done once at most those of tile it+1 remain
+      if (it + 1 < ntiles) td.wait_older(); else td.wait_all();
+      tile_barrier();
+      // buffer (it+2) % 3 was last read in iteration it-1, which every wave has left
+      if (it + 2 < ntiles) td.load(krs, srs, it + 2, ktile[(it + 2) % 3], lane);
+      const uint8_t* kt = ktile[it % 3];
       const int s0 = it * kTileKeys;
       if (s0 <= tlim) {
-        float sc = tile_scores<DT, D, HT>(rs, &ktile[it & 1][0], C::PITCH, lane);
+        float sc = tile_scores<DT, D, HT>(rs, kt, C::PITCH, lane);
         const int s = s0 + lane;
-        if constexpr (DT == DT_FP8) sc *= __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, lane * 4, s0 * 4, 0));
+        if constexpr (DT == DT_FP8) sc *= *(const float*)(kt + C::TILE_BYTES + lane * 4);
         const uint32_t u = order_key(sc);
         if (cnt + 64 > kCandCap) {
           __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
@@ -538,7 +666,6 @@ __global__ __launch_bounds__(256, 2) void ix_topk_kernel(IxParams p, uint32_t* w
         }
         cnt += __builtin_popcountll(m);
       }
-      if (it + 1 < ntiles) tc.store(ktile[(it + 1) & 1], pre);
     }
     if (vrow) {
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
@@ -566,7 +693,7 @@ constexpr int kScanSlice = kTileKeys * kScanStagesPerWave * 4;
 template <int DT, int D, int HT>
 __global__ __launch_bounds__(256, 2) void ix_scan_kernel(IxParams p) {
   typedef Cfg<DT, D> C;
-  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wid = wave_id(), lane = threadIdx.x & 63;
   const int64_t gi = blockIdx.y;                  // flattened (batch, query row)
   const int b = (int)(gi / p.n_q);
   const int64_t i = gi % p.n_q;
