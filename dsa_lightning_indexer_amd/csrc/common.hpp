@@ -93,9 +93,10 @@ hipError_t indexer_scores_f32(const dsa_indexer_args& a, int64_t row0, int64_t r
                               int64_t out_row_stride, hipStream_t s);
 hipError_t indexer_scores_mfma(const dsa_indexer_args& a, int64_t row0, int64_t rows, float* out,
                                hipStream_t s);
-// Fused prefill INDEXER + Top-k: persistent grid of at most kTopkSlots workgroups,
-// each with a private candidate slice in the workspace (topk_fused_ws_bytes()).
-constexpr int kTopkSlots = 512;
+// Fused prefill INDEXER + Top-k: persistent grid with one query row per wave;
+// each of at most kTopkWaveSlots waves owns a candidate slice in the workspace
+// (topk_fused_ws_bytes()).
+constexpr int kTopkWaveSlots = 2048;
 size_t topk_fused_ws_bytes();
 hipError_t indexer_topk_fused(const dsa_indexer_args& a, int32_t k, int32_t* idx, void* ws, hipStream_t s);
 // Decode-shaped scan: fp32 scores of every (row, s) into `scores` [batch*n_q, n_k] and the

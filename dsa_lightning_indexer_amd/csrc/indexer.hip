@@ -32,7 +32,11 @@ enum { DT_BF16 = 1, DT_FP8 = 2 };
 enum { MODE_SCORES = 0, MODE_TOPK = 1 };
 
 constexpr int kTileKeys = 64;
-constexpr int kRowsPerBlock = 4;       // one query row per wave
+constexpr int kRowsPerBlock = 4;       // scores kernel: one query row per wave
+// fused kernel: one query row per wave, kTopkWaves rows per workgroup
+constexpr int kTopkWaves = 4;
+constexpr int kTopkThreads = 64 * kTopkWaves;
+constexpr int kTopkBlocksPerCu = 8 / kTopkWaves;   // two waves per SIMD
 
 struct IxParams {
   const void* q;
@@ -255,32 +259,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Per-thread, loop-invariant offsets of the tile copy: chunk j of thread tid is
-// 16-byte part (c % CPR) of key (c / CPR), c = tid + 256 j.
-template <int DT, int D>
-struct TileCopy {
-  typedef Cfg<DT, D> C;
-  uint32_t goff[C::NCH];   // byte offset inside a tile of k rows in HBM
-  uint32_t loff[C::NCH];   // byte offset inside an LDS tile
-  __device__ __forceinline__ TileCopy() {
-#pragma unroll
-    for (int j = 0; j < C::NCH; ++j) {
-      const int c = threadIdx.x + 256 * j;
-      goff[j] = (uint32_t)((c / C::CPR) * C::ROWB + (c % C::CPR) * 16);
-      loff[j] = (uint32_t)((c / C::CPR) * C::PITCH + (c % C::CPR) * 16);
-    }
-  }
-  // keys at or past the buffer's end read as zero
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int tile, i32x4 (&pre)[C::NCH]) const {
-    const int soff = tile * kTileKeys * C::ROWB;
-#pragma unroll
-    for (int j = 0; j < C::NCH; ++j) pre[j] = __builtin_amdgcn_raw_buffer_load_b128(r, goff[j], soff, 0);
-  }
-  __device__ __forceinline__ void store(uint8_t* dst, const i32x4 (&pre)[C::NCH]) const {
-#pragma unroll
-    for (int j = 0; j < C::NCH; ++j) *(i32x4*)(dst + loff[j]) = pre[j];
-  }
-};
 
 // One buffer_load ... lds of `bytes` (4 or 16) per lane at byte offset voff,
 // landing at LDS address lds + bytes * lane.  Issued from inline asm so that
@@ -309,23 +287,23 @@ __device__ __forceinline__ void tile_barrier() {
 // one such load writes LDS bytes [base + 16 l, base + 16 l + 16), so a tile of
 // PITCH-byte rows (ROWB data bytes + 16 pad bytes) is SPR = CPR + 1 loads of 64
 // 16-byte slots: slot q holds part q % SPR of row q / SPR, and pad slots read
-// past the buffer's end (zeros).  Load j of a tile is issued by wave j % 4.
+// past the buffer's end (zeros).  Load j of a tile is issued by wave j % W.
 // Offsets go in the per-lane offset so that the buffer's range check covers
 // them: keys at or past the end of the range read as zero.
-template <int DT, int D>
+template <int DT, int D, int W>
 struct TileDma {
   typedef Cfg<DT, D> C;
   static constexpr int SPR = C::CPR + 1;
   static constexpr int NI = SPR + (DT == DT_FP8 ? 1 : 0);   // + one 4-byte-per-lane load of the key scales
-  static constexpr int NPW = (NI + 3) / 4;           // loads per wave and tile, at most
+  static constexpr int NPW = (NI + W - 1) / W;       // loads per wave and tile, at most (W waves)
   uint32_t goff[NPW];
   int nload;                                          // loads this wave issues per tile
   int wid;
   __device__ __forceinline__ TileDma(int wid_, int lane) : wid(wid_) {
-    nload = (NI - wid_ + 3) / 4;
+    nload = (NI - wid_ + W - 1) / W;
 #pragma unroll
     for (int m = 0; m < NPW; ++m) {
-      const int q = 64 * (wid_ + 4 * m) + lane;
+      const int q = 64 * (wid_ + W * m) + lane;
       const int row = q / SPR, part = q % SPR;
       goff[m] = part < C::CPR ? (uint32_t)(row * C::ROWB + part * 16) : 0x80000000u;
     }
@@ -336,7 +314,7 @@ struct TileDma {
     const uint32_t toff = (uint32_t)tile * (kTileKeys * C::ROWB);
 #pragma unroll
     for (int m = 0; m < NPW; ++m) {
-      const int j = wid + 4 * m;
+      const int j = wid + W * m;
       if (j < SPR) {
         lds_dma<16>(r, dst + j * 1024, goff[m] + toff);
       } else if (DT == DT_FP8 && j == SPR) {
@@ -344,15 +322,20 @@ struct TileDma {
       }
     }
   }
-  // Wait until this wave's loads of the older of two tiles in flight are done
-  // (loads complete in issue order; the wave issues NPW or NPW-1 per tile).
-  __device__ __forceinline__ void wait_older() const {
-    // s_waitcnt encoding (gfx9): vmcnt in bits 3:0 (NPW <= 5 here); expcnt and lgkmcnt at their maxima
-    static_assert(NPW >= 1 && NPW <= 15, "vmcnt field");
-    if (nload == NPW) __builtin_amdgcn_s_waitcnt(0x0F70 | NPW);
-    else __builtin_amdgcn_s_waitcnt(0x0F70 | (NPW - 1));
+  // Wait until this wave's loads of the oldest tile in flight are done while
+  // those of `younger` later tiles may still run (loads complete in issue
+  // order; the wave issues NPW or NPW-1 loads per tile).
+  __device__ __forceinline__ void wait_oldest(int younger) const {
+    const int n = younger * (nload == NPW ? NPW : NPW - 1);
+    // s_waitcnt encoding (gfx9): vmcnt in bits 3:0; expcnt and lgkmcnt at their maxima
+    switch (n) {
+#define DSA_VMW(c) case c: __builtin_amdgcn_s_waitcnt(0x0F70 | c); break;
+      DSA_VMW(1) DSA_VMW(2) DSA_VMW(3) DSA_VMW(4) DSA_VMW(5) DSA_VMW(6) DSA_VMW(7)
+      DSA_VMW(8) DSA_VMW(9) DSA_VMW(10) DSA_VMW(11) DSA_VMW(12) DSA_VMW(13) DSA_VMW(14) DSA_VMW(15)
+#undef DSA_VMW
+      default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    }
   }
-  __device__ __forceinline__ void wait_all() const { __builtin_amdgcn_s_waitcnt(0x0F70); }
 };
 
 // ---------------------------------------------------------------- wave select
@@ -361,6 +344,7 @@ struct TileDma {
 __device__ __forceinline__ void lds_sync() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup"); }
 
 constexpr int kCandCap = 16384;        // candidates per row before a compaction
+constexpr int kTileStages = 3;         // LDS tile buffers of the fused kernel (prefetch depth + 1)
 
 // Entries [j, j+4) of a candidate array in one 16-byte load.  The arrays are
 // 16-byte aligned and their capacity is a multiple of 4, so a load that starts
@@ -584,23 +568,24 @@ __global__ __launch_bounds__(256, 2) void ix_scores_kernel(IxParams p) {
 // block of 4 query rows (heaviest rows first) from a device counter; blockIdx.x
 // names its private candidate slice in the workspace.
 template <int DT, int D, int HT>
-__global__ __launch_bounds__(256, 2) void ix_topk_kernel(IxParams p, uint32_t* work, uint32_t* cand) {
+__global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk_kernel(IxParams p, uint32_t* work,
+                                                                                    uint32_t* cand) {
   typedef Cfg<DT, D> C;
-  // three staging buffers: tiles it+1 and it+2 load while tile it is scored
-  __shared__ __attribute__((aligned(16))) uint8_t ktile[3][C::BUF_BYTES];
-  __shared__ uint32_t hist[kRowsPerBlock][256];
+  // staging buffers: tiles it+1 .. it+kTileStages-1 load while tile it is scored
+  __shared__ __attribute__((aligned(16))) uint8_t ktile[kTileStages][C::BUF_BYTES];
+  __shared__ uint32_t hist[kTopkWaves][256];
   __shared__ int64_t s_item;
 
   const int wid = wave_id(), lane = threadIdx.x & 63;
-  uint32_t* cu = cand + ((size_t)blockIdx.x * kRowsPerBlock + wid) * 2 * kCandCap;
+  uint32_t* cu = cand + ((size_t)blockIdx.x * kTopkWaves + wid) * 2 * kCandCap;
   uint32_t* ci = cu + kCandCap;
   // candidate slice as a buffer: appends are 32-bit offsets (keys at [0, cap),
   // positions at [cap, 2 cap))
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(cu, 2u * kCandCap * 4u);
-  const int64_t nrb = (p.rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int64_t nrb = (p.rows + kTopkWaves - 1) / kTopkWaves;
   const int64_t total = nrb * p.batch;
   const int k = p.topk;
-  const TileDma<DT, D> td(wid, lane);
+  const TileDma<DT, D, kTopkWaves> td(wid, lane);
 
   for (;;) {
     if (threadIdx.x == 0) s_item = (int64_t)atomicAdd(work, 1u);
@@ -610,13 +595,13 @@ __global__ __launch_bounds__(256, 2) void ix_topk_kernel(IxParams p, uint32_t* w
     if (item >= total) break;
     const int b = (int)(item % p.batch);
     const int64_t rb = nrb - 1 - item / p.batch;                 // heaviest rows first
-    const int64_t rloc0 = rb * kRowsPerBlock;
+    const int64_t rloc0 = rb * kTopkWaves;
     const int64_t rloc = rloc0 + wid;
     const bool vrow = rloc < p.rows;
     const int64_t i = p.row0 + rloc;
     // positions fit in 32 bits (n_k < 2^31)
     const int t = vrow ? (int)(p.q_pos0 + i) : -1;
-    const int64_t rlast = rloc0 + kRowsPerBlock - 1 < p.rows ? rloc0 + kRowsPerBlock - 1 : p.rows - 1;
+    const int64_t rlast = rloc0 + kTopkWaves - 1 < p.rows ? rloc0 + kTopkWaves - 1 : p.rows - 1;
     const int64_t t_last = p.q_pos0 + p.row0 + rlast;
     const int nkeys = (int)(t_last + 1 < p.n_k ? t_last + 1 : p.n_k);
     const int ntiles = (nkeys + kTileKeys - 1) / kTileKeys;
@@ -636,15 +621,18 @@ __global__ __launch_bounds__(256, 2) void ix_topk_kernel(IxParams p, uint32_t* w
     int cnt = 0;
     bool full = false, strict = false;
     uint32_t thr = 0;
-    td.load(krs, srs, 0, ktile[0], lane);
-    if (ntiles > 1) td.load(krs, srs, 1, ktile[1], lane);
+#pragma unroll
+    for (int i = 0; i < kTileStages - 1; ++i)
+      if (i < ntiles) td.load(krs, srs, i, ktile[i], lane);
     for (int it = 0; it < ntiles; ++it) {
-      // this wave's loads of tile it are done once at most those of tile it+1 remain
-      if (it + 1 < ntiles) td.wait_older(); else td.wait_all();
+      // tiles it .. it+younger are in flight; this wave's loads of tile it must be done
+      const int ahead = ntiles - 1 - it;
+      td.wait_oldest(ahead < kTileStages - 2 ? ahead : kTileStages - 2);
       tile_barrier();
-      // buffer (it+2) % 3 was last read in iteration it-1, which every wave has left
-      if (it + 2 < ntiles) td.load(krs, srs, it + 2, ktile[(it + 2) % 3], lane);
-      const uint8_t* kt = ktile[it % 3];
+      // buffer (it-1) % kTileStages was last read in iteration it-1, which every wave has left
+      if (it + kTileStages - 1 < ntiles)
+        td.load(krs, srs, it + kTileStages - 1, ktile[(it + kTileStages - 1) % kTileStages], lane);
+      const uint8_t* kt = ktile[it % kTileStages];
       const int s0 = it * kTileKeys;
       if (s0 <= tlim) {
         float sc = tile_scores<DT, D, HT>(rs, kt, C::PITCH, lane);
@@ -794,8 +782,8 @@ int persistent_blocks() {
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  int nb = 2 * cus;
-  if (nb > dsa_host::kTopkSlots) nb = dsa_host::kTopkSlots;
+  int nb = kTopkBlocksPerCu * cus;
+  if (nb > dsa_host::kTopkWaveSlots / kTopkWaves) nb = dsa_host::kTopkWaveSlots / kTopkWaves;
   cached = nb;
   return nb;
 }
@@ -805,15 +793,15 @@ hipError_t launch_topk_dt(const IxParams& p, void* ws, hipStream_t s) {
   uint32_t* work = (uint32_t*)ws;
   uint32_t* cand = (uint32_t*)((char*)ws + 256);
   hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, s, work, 64);
-  const int64_t nrb = (p.rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int64_t nrb = (p.rows + kTopkWaves - 1) / kTopkWaves;
   int64_t items = nrb * p.batch;
   int64_t nb = persistent_blocks();
   if (nb > items) nb = items;
   dim3 grid((unsigned)nb);
   if (p.heads > 32) {
-    hipLaunchKernelGGL((ix_topk_kernel<DT, D, 2>), grid, dim3(256), 0, s, p, work, cand);
+    hipLaunchKernelGGL((ix_topk_kernel<DT, D, 2>), grid, dim3(kTopkThreads), 0, s, p, work, cand);
   } else {
-    hipLaunchKernelGGL((ix_topk_kernel<DT, D, 1>), grid, dim3(256), 0, s, p, work, cand);
+    hipLaunchKernelGGL((ix_topk_kernel<DT, D, 1>), grid, dim3(kTopkThreads), 0, s, p, work, cand);
   }
   return hipGetLastError();
 }
@@ -871,7 +859,7 @@ hipError_t indexer_scores_mfma(const dsa_indexer_args& a, int64_t row0, int64_t 
 }
 
 size_t topk_fused_ws_bytes() {
-  return 256 + (size_t)kTopkSlots * kRowsPerBlock * 2 * kCandCap * sizeof(uint32_t);
+  return 256 + (size_t)kTopkWaveSlots * 2 * kCandCap * sizeof(uint32_t);
 }
 
 hipError_t indexer_topk_fused(const dsa_indexer_args& a, int32_t k, int32_t* idx, void* ws, hipStream_t s) {
