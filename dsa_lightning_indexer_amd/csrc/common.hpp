@@ -33,6 +33,14 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
 // derived from it, buffer resources and per-wave bases stay in SGPRs.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// Workgroup barrier for LDS data only: waits for this wave's LDS accesses
+// (lgkmcnt) but not for global loads in flight, unlike __syncthreads, whose
+// release fence drains every outstanding vector-memory operation.  The asm
+// keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void sync_lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Lane-mask helpers (wave64).
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));

@@ -113,6 +113,7 @@ __global__ __launch_bounds__(256) void sa_generic_kernel(SAParams p) {
 // ---------------------------------------------------------------- MLA MFMA path
 constexpr int kH = 16;       // query heads per latent row
 constexpr int kTile = 16;    // selected positions per step
+constexpr int kMaxTopk = DSA_MAX_TOPK;   // longest index row
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -259,6 +260,175 @@ __global__ __launch_bounds__(64) void sa_mla_kernel(SAParams p) {
   }
 }
 
+// Four waves per (query row, split of its index row).  Wave w owns latent
+// columns [128w, 128w + 128): four 32-wide K steps of Q.K and the 128 V columns
+// of its slice of the output; waves 0 and 1 also own one of the two rope K
+// steps (columns 512 + 32w ..).  Per 16-position step each wave gathers only
+// its own columns of the 16 rows (registers, two steps ahead), forms its
+// partial S^T, and the four partials meet in LDS (one barrier per step, the
+// partial buffer alternates between steps).  Every wave then runs the same
+// online softmax on the full S^T and multiplies its own V slice, staged in a
+// wave-private LDS tile and read back transposed as in sa_mla_kernel.  The
+// output accumulators are a quarter of sa_mla_kernel's, so three workgroups
+// fit on a CU.
+template <int DQK, int DV>
+__global__ __launch_bounds__(256, 3) void sa_mla4_kernel(SAParams p) {
+  static_assert(DV % 128 == 0 && DQK - DV == 64, "latent layout: 4 V slices of 128 columns + 64 rope columns");
+  constexpr int NW = 4;
+  constexpr int CW = DV / NW;            // V columns per wave
+  constexpr int KSW = CW / 32;           // K steps inside the wave's V slice
+  constexpr int KS = KSW + 1;            // + a rope step (waves 0 and 1)
+  constexpr int NDT = CW / 16;           // output tiles of 16 columns per wave
+  constexpr int VPITCH = CW * 2 + 32;    // LDS row pitch in bytes (bank spread for the transposed reads)
+  __shared__ __attribute__((aligned(16))) uint8_t vt[NW][kTile * VPITCH];
+  __shared__ f32x4 spart[2][NW][64];
+  __shared__ int32_t sidx[kMaxTopk];      // this split's selected positions
+
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id();
+  const int g = lane >> 4, col = lane & 15;
+  const bool rope = w < 2;
+  const int split = (int)(blockIdx.x % p.nsplit);
+  const int64_t gi = blockIdx.x / p.nsplit;          // flattened (batch, query row)
+  const int b = (int)(gi / p.n_q);
+  const int per = (p.topk + p.nsplit - 1) / p.nsplit;
+  const int e0 = split * per;
+  const int e1 = e0 + per < p.topk ? e0 + per : p.topk;
+  // first column (elements) of K step ks of this wave
+  auto kcol = [&](int ks) { return ks < KSW ? CW * w + 32 * ks : DV + 32 * w; };
+
+  // Q^T as the B operand: lane holds head `col`, 8 columns of each K step.
+  bf16x8 qf[KS];
+  const __bf16* qrow = (const __bf16*)p.q + (gi * kH + col) * (int64_t)DQK;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qf[ks] = (ks < KSW || rope) ? *(const bf16x8*)(qrow + kcol(ks) + 8 * g) : bf16x8{};
+
+  f32x4 o[NDT];
+#pragma unroll
+  for (int d = 0; d < NDT; ++d) o[d] = f32x4{};
+  float m_run = -__builtin_inff(), l_run = 0.f;
+
+  // Gathers are buffer loads over this batch's latent rows: a position that is
+  // invalid (or past the split) gets an offset beyond the range and reads
+  // zeros, so every fetch is the same straight-line code and the compiler can
+  // keep two steps of gathers in flight.  Positions come from LDS, not from
+  // vector loads that would have to wait behind the gathers in flight.
+  const __amdgpu_buffer_rsrc_t kvr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>((const void*)((const __bf16*)p.kv + (int64_t)b * p.kv_bs)), (short)0,
+      (int)((int64_t)p.n_k * DQK * 2), 0x00020000);
+  {
+    const int32_t* ir = p.idx + gi * (int64_t)p.topk;
+    for (int e = e0 + (int)threadIdx.x; e < e1; e += NW * 64) sidx[e - e0] = ir[e];
+  }
+  __syncthreads();
+  uint8_t* wrow = vt[w] + col * VPITCH + 16 * g;
+  const uint8_t* rbase = vt[w] + (4 * g + (col >> 2)) * VPITCH + 8 * (col & 3);
+  int pbuf = 0;
+
+  auto fetch = [&](int tb, bf16x8 (&kb)[KS], uint64_t& vm) {
+    const int e = tb + col;
+    const int32_t s = sidx[(e < e1 ? e : e1 - 1) - e0];
+    const bool valid = e < e1 && s >= 0 && s < p.n_k;
+    vm = ballot(valid);
+    const uint32_t base = valid ? (uint32_t)s * (DQK * 2) : 0x80000000u;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t off = (ks < KSW || rope ? base : 0x80000000u) + (uint32_t)(kcol(ks) * 2 + 16 * g);
+      kb[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kvr, off, 0, 0));
+    }
+  };
+  auto step = [&](const bf16x8 (&kb)[KS], uint64_t vm) {
+    f32x4 acc = f32x4{};
+#pragma unroll
+    for (int ks = 0; ks < KSW; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[ks], qf[ks], acc, 0, 0, 0);
+    if (rope) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[KSW], qf[KSW], acc, 0, 0, 0);
+#pragma unroll
+    for (int ks = 0; ks < KSW; ++ks) *(bf16x8*)(wrow + 64 * ks) = kb[ks];
+    spart[pbuf][w][lane] = acc;
+    sync_lds_barrier();
+    // the same summation order in every wave: identical softmax state everywhere
+    const f32x4 sc = ((spart[pbuf][0][lane] + spart[pbuf][1][lane]) + spart[pbuf][2][lane]) + spart[pbuf][3][lane];
+    pbuf ^= 1;
+    // sc[i]: head `col`, position 4*g + i of this step.
+    float z[4];
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] = ((vm >> (4 * g + i)) & 1ull) ? sc[i] * p.scale : -__builtin_inff();
+      mx = fmaxf(mx, z[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    bf16x4 pb_hi = bf16x4{}, pb_lo = bf16x4{};
+    float alpha = 1.f;
+    if (m_new != -__builtin_inff()) {
+      alpha = (m_run == m_new) ? 1.f : ((m_run == -__builtin_inff()) ? 0.f : __expf(m_run - m_new));
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pe = z[i] == -__builtin_inff() ? 0.f : __expf(z[i] - m_new);
+        const __bf16 hi = (__bf16)pe;
+        pb_hi[i] = hi;
+        pb_lo[i] = (__bf16)(pe - (float)hi);
+        ps += pe;
+      }
+      l_run = l_run * alpha + ps;
+      m_run = m_new;
+    }
+    if (ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(rbase + 32 * dt));
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_hi, o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_lo, o[dt], 0, 0, 0);
+    }
+    // this wave's V tile is rewritten next step only after these reads returned
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  };
+
+  // three register buffers, rotated by unrolling the loop by three steps;
+  // fetches past the split read zeros without touching memory
+  bf16x8 kbA[KS], kbB[KS], kbC[KS];
+  uint64_t vmA = 0, vmB = 0, vmC = 0;
+  if (e0 < e1) {
+    fetch(e0, kbA, vmA);
+    fetch(e0 + kTile, kbB, vmB);
+  }
+  for (int tb = e0; tb < e1; tb += 3 * kTile) {
+    fetch(tb + 2 * kTile, kbC, vmC);
+    step(kbA, vmA);
+    if (tb + kTile >= e1) break;
+    fetch(tb + 3 * kTile, kbA, vmA);
+    step(kbB, vmB);
+    if (tb + 2 * kTile >= e1) break;
+    fetch(tb + 4 * kTile, kbB, vmB);
+    step(kbC, vmC);
+  }
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  // O^T layout: lane holds head `col`, columns CW*w + 16*dt + 4*g + (0..3)
+  if (p.nsplit == 1) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    float* out = p.out + (gi * kH + col) * (int64_t)DV + CW * w + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) *(f32x4*)(out + 16 * dt) = o[dt] * inv;
+  } else {
+    float* wo = p.ws_o + ((gi * p.nsplit + split) * kH + col) * (int64_t)DV + CW * w + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) *(f32x4*)(wo + 16 * dt) = o[dt];
+    if (w == 0 && g == 0) {
+      float* ml = p.ws_ml + ((gi * p.nsplit + split) * kH + col) * 2;
+      ml[0] = m_run;
+      ml[1] = l_run;
+    }
+  }
+}
+
 // Merge the split partials of one (query row, head): weights exp(m_s - M) are
 // computed once into LDS, then each thread accumulates its output columns.
 __global__ __launch_bounds__(256) void sa_combine_kernel(SAParams p) {
@@ -295,8 +465,9 @@ __global__ __launch_bounds__(256) void sa_combine_kernel(SAParams p) {
 }
 
 bool mla_ok(const dsa_sparse_attn_args& a) {
+  // (one batch's latent rows are addressed with 32-bit byte offsets)
   return a.dtype == DSA_BF16 && a.heads == kH && a.kv_heads == 1 && a.d_qk == 576 &&
-         a.d_v == 512 && a.v == nullptr;
+         a.d_v == 512 && a.v == nullptr && (int64_t)a.n_k * a.d_qk * 2 < ((int64_t)1 << 31);
 }
 
 int pick_nsplit(const dsa_sparse_attn_args& a) {
@@ -343,7 +514,7 @@ hipError_t sparse_attn_launch(const dsa_sparse_attn_args& a, void* ws, hipStream
       p.ws_ml = p.ws_o + rows * p.nsplit * a.heads * (int64_t)a.d_v;
     }
     dim3 grid((unsigned)(rows * p.nsplit));
-    hipLaunchKernelGGL((sa_mla_kernel<576, 512>), grid, dim3(64), 0, s, p);
+    hipLaunchKernelGGL((sa_mla4_kernel<576, 512>), grid, dim3(256), 0, s, p);
     if (p.nsplit > 1) {
       hipLaunchKernelGGL(sa_combine_kernel, dim3((unsigned)(rows * a.heads)), dim3(256), 0, s, p);
     }
