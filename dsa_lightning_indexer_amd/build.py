@@ -27,7 +27,7 @@ FLAGS = [
 # NaN-quieting v_max plus the max.
 # MFMA results stay in VGPRs (the VALU epilogue reads them directly instead of
 # copying them out of AGPRs).
-EXTRA = {"indexer.hip": ["-fno-honor-nans"], "sparse_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+EXTRA = {"indexer.hip": ["-fno-honor-nans"], "sparse_attn.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src):

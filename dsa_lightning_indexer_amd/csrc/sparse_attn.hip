@@ -3,20 +3,23 @@
 //
 //  * sa_generic_kernel  any shape, fp32 or bf16, one workgroup per (query row,
 //    head): logits in LDS, block max/sum, then P.V with coalesced V reads.
-//  * sa_mla_kernel      bf16 MLA latent layout on MFMA: 16 query heads share one
+//  * sa_mla4_kernel     bf16 MLA latent layout on MFMA: 16 query heads share one
 //    576-wide latent row per position whose first 512 columns are V.  One
-//    workgroup per (query row, split of the index row); each wave takes 16
-//    selected positions at a time:
-//      S^T[16 keys x 16 heads] = K_sel . Q^T     (16x16x32 bf16 MFMA, K rows
-//                                                 gathered straight from HBM)
+//    four-wave workgroup per (query row, split of the index row); per step of
+//    16 selected positions:
+//      S^T[16 keys x 16 heads] = K_sel . Q^T    (16x16x32 bf16 MFMA; each wave
+//                                                contracts its own columns of
+//                                                the gathered rows, partials
+//                                                are summed through LDS)
 //      online softmax per head (the S^T layout gives each lane one head)
-//      O^T[512 x 16] += V_sel^T . P^T           (16x16x16 bf16 MFMA; V^T comes
-//                                                 from the gathered rows via LDS)
+//      O^T[128 x 16] += V_sel^T . P^T          (16x16x16 bf16 MFMA per wave on
+//                                                its 128 V columns; V^T comes
+//                                                from the gathered rows via a
+//                                                transposing LDS read)
 //    P^T needs no data movement: the S^T accumulator layout (lane = head,
 //    registers = 4 consecutive keys) is exactly the B-operand layout of the
-//    16x16x16 MFMA.  Waves are merged in LDS at the end; with several splits
-//    per row the partial (max, sum, O) go to the workspace and
-//    sa_combine_kernel merges them.
+//    16x16x16 MFMA.  With several splits per row the partial (max, sum, O) go
+//    to the workspace and sa_combine_kernel merges them.
 #include "common.hpp"
 
 namespace {
@@ -53,6 +56,38 @@ __device__ float block_reduce(float v, float* sh, bool is_max) {
   for (int w = 1; w < nw; ++w) r = is_max ? fmaxf(r, sh[w]) : r + sh[w];
   __syncthreads();
   return r;
+}
+
+// max / sum over lanes l, l^16, l^32, l^48 (the four lanes holding one head in
+// the 16x16 MFMA layouts), with lane swaps instead of LDS permutes
+__device__ __forceinline__ float quad_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Weights p (4 per lane) as bf16 hi + lo parts: hi = bf16(p), lo = bf16(p - hi),
+// converted two at a time.
+__device__ __forceinline__ void split_bf16(const float (&pe)[4], bf16x4& hi, bf16x4& lo) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const bf16x2 h = __builtin_convertvector((f32x2){pe[2 * j], pe[2 * j + 1]}, bf16x2);
+    const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+    const float h0 = __uint_as_float(hb << 16), h1 = __uint_as_float(hb & 0xffff0000u);
+    const bf16x2 l = __builtin_convertvector((f32x2){pe[2 * j] - h0, pe[2 * j + 1] - h1}, bf16x2);
+    hi[2 * j] = h[0]; hi[2 * j + 1] = h[1];
+    lo[2 * j] = l[0]; lo[2 * j + 1] = l[1];
+  }
 }
 
 // ---------------------------------------------------------------- generic path
@@ -117,149 +152,6 @@ constexpr int kMaxTopk = DSA_MAX_TOPK;   // longest index row
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-// One wave per (query row, split of its index row).  Per 16-position step:
-//   1. the 16 gathered latent rows arrive in registers as the A operand of
-//      S^T = K_sel . Q^T (16x16x32 bf16 MFMA, lane = position l%16, 8 columns);
-//      the next step's rows are already being fetched (register double buffer);
-//   2. their first DV columns are stored to a row-major LDS tile (16-byte
-//      writes) and read back transposed with ds_read_b64_tr_b16, which hands
-//      every lane V[4g..4g+3][d0 + l%16] -- the V^T A operand of the 16x16x16
-//      MFMA -- when lane s of lane group g points at V[4g + s/4][d0 + 4(s%4)];
-//   3. online softmax per head: the S^T accumulator puts one head per lane and
-//      4 consecutive positions in its registers, which is already the P^T B
-//      operand; P is split into bf16 hi + lo so P.V keeps ~2^-17 relative
-//      accuracy of the weights;
-//   4. O^T[DV x 16] += V^T . P^T; rescaling of O is skipped when no head's
-//      running max moved.
-template <int DQK, int DV>
-__global__ __launch_bounds__(64) void sa_mla_kernel(SAParams p) {
-  constexpr int NKS = DQK / 32;        // 16x16x32 K steps for Q.K
-  constexpr int NVS = DV / 32;         // K steps whose 8-column slices are V columns
-  constexpr int NDT = DV / 16;         // output tiles of 16 V columns
-  constexpr int PITCH = DV * 2 + 32;   // LDS row pitch in bytes (bank spread)
-  __shared__ __attribute__((aligned(16))) uint8_t vt[kTile * PITCH];
-
-  const int lane = threadIdx.x;
-  const int g = lane >> 4, col = lane & 15;
-  const int split = (int)(blockIdx.x % p.nsplit);
-  const int64_t gi = blockIdx.x / p.nsplit;          // flattened (batch, query row)
-  const int b = (int)(gi / p.n_q);
-  const int per = (p.topk + p.nsplit - 1) / p.nsplit;
-  const int e0 = split * per;
-  const int e1 = e0 + per < p.topk ? e0 + per : p.topk;
-
-  // Q^T as the B operand: lane holds head `col`, columns 32*ks + 8*g .. +8.
-  bf16x8 qf[NKS];
-  const __bf16* qrow = (const __bf16*)p.q + (gi * kH + col) * (int64_t)DQK;
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8*)(qrow + 32 * ks + 8 * g);
-
-  f32x4 o[NDT];
-#pragma unroll
-  for (int d = 0; d < NDT; ++d) o[d] = f32x4{};
-  float m_run = -__builtin_inff(), l_run = 0.f;
-
-  const __bf16* kvb = (const __bf16*)p.kv + (int64_t)b * p.kv_bs;
-  const int32_t* ir = p.idx + gi * (int64_t)p.topk;
-  // this lane's write slot and transposed-read address inside the LDS tile
-  uint8_t* wrow = vt + col * PITCH + 16 * g;
-  const uint8_t* rbase = vt + (4 * g + (col >> 2)) * PITCH + 8 * (col & 3);
-
-  // Gather the 16 latent rows of the step starting at entry tb into kb (zeros for
-  // invalid entries); vm gets the valid-position mask.
-  auto fetch = [&](int tb, bf16x8 (&kb)[NKS], uint64_t& vm) {
-    const int e = tb + col;
-    const int32_t s = e < e1 ? ir[e] : -1;
-    const bool valid = s >= 0 && s < p.n_k;
-    vm = ballot(valid);
-    const __bf16* rowp = kvb + (int64_t)(valid ? s : 0) * DQK;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) kb[ks] = valid ? *(const bf16x8*)(rowp + 32 * ks + 8 * g) : bf16x8{};
-  };
-  auto step = [&](const bf16x8 (&kb)[NKS], uint64_t vm) {
-    f32x4 acc = f32x4{};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[ks], qf[ks], acc, 0, 0, 0);
-#pragma unroll
-    for (int ks = 0; ks < NVS; ++ks) *(bf16x8*)(wrow + 64 * ks) = kb[ks];
-    // acc[i]: head `col`, position 4*g + i of this step.
-    float z[4];
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[i] = ((vm >> (4 * g + i)) & 1ull) ? acc[i] * p.scale : -__builtin_inff();
-      mx = fmaxf(mx, z[i]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    bf16x4 pb_hi = bf16x4{}, pb_lo = bf16x4{};
-    float alpha = 1.f;
-    if (m_new != -__builtin_inff()) {
-      alpha = (m_run == m_new) ? 1.f : ((m_run == -__builtin_inff()) ? 0.f : __expf(m_run - m_new));
-      float ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pe = z[i] == -__builtin_inff() ? 0.f : __expf(z[i] - m_new);
-        const __bf16 hi = (__bf16)pe;
-        pb_hi[i] = hi;
-        pb_lo[i] = (__bf16)(pe - (float)hi);
-        ps += pe;
-      }
-      l_run = l_run * alpha + ps;
-      m_run = m_new;
-    }
-    if (ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(rbase + 32 * dt));
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_hi, o[dt], 0, 0, 0);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_lo, o[dt], 0, 0, 0);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  };
-
-  // three register buffers (two steps of gathers in flight while one computes),
-  // rotated by unrolling the loop by three steps
-  bf16x8 kbA[NKS], kbB[NKS], kbC[NKS];
-  uint64_t vmA = 0, vmB = 0, vmC = 0;
-  if (e0 < e1) fetch(e0, kbA, vmA);
-  if (e0 + kTile < e1) fetch(e0 + kTile, kbB, vmB);
-  for (int tb = e0; tb < e1; tb += 3 * kTile) {
-    if (tb + 2 * kTile < e1) fetch(tb + 2 * kTile, kbC, vmC);
-    step(kbA, vmA);
-    if (tb + kTile >= e1) break;
-    if (tb + 3 * kTile < e1) fetch(tb + 3 * kTile, kbA, vmA);
-    step(kbB, vmB);
-    if (tb + 2 * kTile >= e1) break;
-    if (tb + 4 * kTile < e1) fetch(tb + 4 * kTile, kbB, vmB);
-    step(kbC, vmC);
-  }
-  // row sum of head `col` = the sum over the 4 lanes holding it
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
-  // O^T layout: lane holds head `col`, columns 16*dt + 4*g + (0..3)
-  if (p.nsplit == 1) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    float* out = p.out + (gi * kH + col) * (int64_t)DV + 4 * g;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) *(f32x4*)(out + 16 * dt) = o[dt] * inv;
-  } else {
-    float* wo = p.ws_o + ((gi * p.nsplit + split) * kH + col) * (int64_t)DV + 4 * g;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) *(f32x4*)(wo + 16 * dt) = o[dt];
-    if (g == 0) {
-      float* ml = p.ws_ml + ((gi * p.nsplit + split) * kH + col) * 2;
-      ml[0] = m_run;
-      ml[1] = l_run;
-    }
-  }
-}
-
 // Four waves per (query row, split of its index row).  Wave w owns latent
 // columns [128w, 128w + 128): four 32-wide K steps of Q.K and the 128 V columns
 // of its slice of the output; waves 0 and 1 also own one of the two rope K
@@ -308,6 +200,7 @@ __global__ __launch_bounds__(256, 3) void sa_mla4_kernel(SAParams p) {
 #pragma unroll
   for (int d = 0; d < NDT; ++d) o[d] = f32x4{};
   float m_run = -__builtin_inff(), l_run = 0.f;
+  const float sl2 = p.scale * 1.4426950408889634f;   // scale * log2(e)
 
   // Gathers are buffer loads over this batch's latent rows: a position that is
   // invalid (or past the split) gets an offset beyond the range and reads
@@ -340,9 +233,9 @@ __global__ __launch_bounds__(256, 3) void sa_mla4_kernel(SAParams p) {
   };
   auto step = [&](const bf16x8 (&kb)[KS], uint64_t vm) {
     f32x4 acc = f32x4{};
+    // (waves 2 and 3 run the rope step on zero operands: same code in every wave)
 #pragma unroll
-    for (int ks = 0; ks < KSW; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[ks], qf[ks], acc, 0, 0, 0);
-    if (rope) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[KSW], qf[KSW], acc, 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[ks], qf[ks], acc, 0, 0, 0);
 #pragma unroll
     for (int ks = 0; ks < KSW; ++ks) *(bf16x8*)(wrow + 64 * ks) = kb[ks];
     spart[pbuf][w][lane] = acc;
@@ -350,31 +243,23 @@ __global__ __launch_bounds__(256, 3) void sa_mla4_kernel(SAParams p) {
     // the same summation order in every wave: identical softmax state everywhere
     const f32x4 sc = ((spart[pbuf][0][lane] + spart[pbuf][1][lane]) + spart[pbuf][2][lane]) + spart[pbuf][3][lane];
     pbuf ^= 1;
-    // sc[i]: head `col`, position 4*g + i of this step.
+    // sc[i]: head `col`, position 4*g + i of this step.  The softmax runs in
+    // base 2 (scores times scale * log2 e; the weights are unchanged).
+    const uint32_t vb = (uint32_t)(vm >> (4 * g));
     float z[4];
-    float mx = -__builtin_inff();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[i] = ((vm >> (4 * g + i)) & 1ull) ? sc[i] * p.scale : -__builtin_inff();
-      mx = fmaxf(mx, z[i]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    for (int i = 0; i < 4; ++i) z[i] = ((vb >> i) & 1u) ? sc[i] * sl2 : -__builtin_inff();
+    const float mx = quad_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
     const float m_new = fmaxf(m_run, mx);
     bf16x4 pb_hi = bf16x4{}, pb_lo = bf16x4{};
     float alpha = 1.f;
     if (m_new != -__builtin_inff()) {
-      alpha = (m_run == m_new) ? 1.f : ((m_run == -__builtin_inff()) ? 0.f : __expf(m_run - m_new));
-      float ps = 0.f;
+      alpha = (m_run == m_new) ? 1.f : ((m_run == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new));
+      float pe[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pe = z[i] == -__builtin_inff() ? 0.f : __expf(z[i] - m_new);
-        const __bf16 hi = (__bf16)pe;
-        pb_hi[i] = hi;
-        pb_lo[i] = (__bf16)(pe - (float)hi);
-        ps += pe;
-      }
-      l_run = l_run * alpha + ps;
+      for (int i = 0; i < 4; ++i) pe[i] = z[i] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(z[i] - m_new);
+      split_bf16(pe, pb_hi, pb_lo);
+      l_run = l_run * alpha + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
       m_run = m_new;
     }
     if (ballot(alpha != 1.f)) {
@@ -409,8 +294,7 @@ __global__ __launch_bounds__(256, 3) void sa_mla4_kernel(SAParams p) {
     fetch(tb + 4 * kTile, kbB, vmB);
     step(kbC, vmC);
   }
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
+  l_run = quad_sum(l_run);
   // O^T layout: lane holds head `col`, columns CW*w + 16*dt + 4*g + (0..3)
   if (p.nsplit == 1) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
@@ -422,8 +306,9 @@ __global__ __launch_bounds__(256, 3) void sa_mla4_kernel(SAParams p) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) *(f32x4*)(wo + 16 * dt) = o[dt];
     if (w == 0 && g == 0) {
+      // the combine step works in natural-log units
       float* ml = p.ws_ml + ((gi * p.nsplit + split) * kH + col) * 2;
-      ml[0] = m_run;
+      ml[0] = m_run * 0.6931471805599453f;
       ml[1] = l_run;
     }
   }
