@@ -45,6 +45,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-report", action="store_true", help="skip the all-F comparison and overlap matrix")
+    p.add_argument("--profile", choices=["indexer", "copy"], default=None,
+                   help="counter-collection runs: 'indexer' launches only the prefill F layer's fused "
+                        "indexer+Top-k (3 launches, the first a warm-up); 'copy' runs a 1 GiB read + "
+                        "1 GiB write elementwise kernel, the calibration for the HBM byte counters")
     return p.parse_args()
 
 
@@ -120,17 +124,75 @@ def cpu_baseline(ix, topk, seconds):
                       f"{pairs} causal pairs in {dt:.1f} s, float64 NumPy"}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_indexer_topk_bf16_L131072_traffic.md")
+
+
+def kernel_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("indexer.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "dsa_lightning_indexer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per fused-kernel launch from the committed counter summary, or
+    None when it is missing or was taken on other kernel sources."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def profile_run(args, dev):
+    if args.profile == "copy":
+        n = 1 << 28                                      # 2^28 floats = 1 GiB
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print("profile copy: 2 launches of a 1 GiB read + 1 GiB write kernel", flush=True)
+        return
+    import dsa_lightning_indexer_amd as dsa
+    from synth import inputs as syn
+    L = args.prefill_len
+    ix = syn.c4_stack(L=L, n_layers=1, seed=4, device=dev, with_sa=False)[0][0]   # the step's first F layer
+    out = torch.empty((1, L, 2048), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    for i in range(3):
+        dsa.topk(ix.q, ix.k, ix.w, 2048, out=out)
+        torch.cuda.synchronize()
+        print(f"profile indexer: fused indexer+Top-k L={L} launch {i + 1}/3 done", flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.profile:
+        profile_run(args, dev)
+        return
     import dsa_lightning_indexer_amd as dsa
     from synth import inputs as syn
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     topk = 2048
     L = args.prefill_len
     pattern_p = "FSSSFSSS"
@@ -181,6 +243,7 @@ def main():
     flop_layer = pairs_layer * 2 * 64 * 128
     achieved_tflops = flop_layer / (k_ms * 1e-3) / 1e12
     log(f"fused indexer+Top-k L={L}: {k_ms:.2f} ms/launch, {achieved_tflops:.1f} TFLOP/s")
+    traffic = measured_traffic() if L == 131072 else None
 
     # decode F-layer indexer+Top-k (scan + select) and one decode attention layer
     dF = [i for i, c in enumerate(pattern_d) if c == "F"][0]
@@ -233,7 +296,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved_tflops / PEAK_BF16_TFLOPS,
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_per_launch": f"{pairs_layer} causal pairs x 16384 flop = {flop_layer:.4g} flop",
             "launch_ms": k_ms,
         },

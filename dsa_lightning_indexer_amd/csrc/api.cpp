@@ -142,7 +142,7 @@ dsa_status run_topk(const dsa_indexer_args* a, const float* scores, int32_t k, i
     if (path == PATH_F32) {
       e = dsa_host::indexer_scores_f32(*a, 0, a->n_q, buf, a->n_k, s);
     } else {
-      e = dsa_host::indexer_scan(*a, buf, sel_ws, k, s);
+      e = dsa_host::indexer_scan(*a, buf, s);
     }
     if (e != hipSuccess) return hip_status(e, "indexer scoring launch");
     sc = buf;

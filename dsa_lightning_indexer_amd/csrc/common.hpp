@@ -107,10 +107,8 @@ hipError_t indexer_scores_mfma(const dsa_indexer_args& a, int64_t row0, int64_t 
 constexpr int kTopkWaveSlots = 2048;
 size_t topk_fused_ws_bytes();
 hipError_t indexer_topk_fused(const dsa_indexer_args& a, int32_t k, int32_t* idx, void* ws, hipStream_t s);
-// Decode-shaped scan: fp32 scores of every (row, s) into `scores` [batch*n_q, n_k] and the
-// first select histogram into the select workspace `sel_ws` (already prepared).
-hipError_t indexer_scan(const dsa_indexer_args& a, float* scores, void* sel_ws, int32_t k,
-                        hipStream_t s);
+// Decode-shaped scan: fp32 scores of every (row, s) into `scores` [batch*n_q, n_k].
+hipError_t indexer_scan(const dsa_indexer_args& a, float* scores, hipStream_t s);
 bool indexer_mfma_supported(const dsa_indexer_args& a);
 
 size_t sparse_attn_ws_bytes(const dsa_sparse_attn_args& a);

@@ -228,6 +228,13 @@ __device__ __forceinline__ float tile_scores(const RowState<DT, D, HT>& rs, cons
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
+// Half-wave combine of the two 32-key subtiles' partials (lanes l and l^32
+// hold complementary head rows of the same key column): lane l ends with key l.
+__device__ __forceinline__ float combine_halves(float p0, float p1) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
 // Cooperative 256-thread copy of the 64-key tile `tile` into registers, then LDS
 // (rows of PITCH bytes).  Keys at or past n_k read as zero.
 template <int DT, int D>
@@ -694,27 +701,43 @@ __global__ __launch_bounds__(256, 2) void ix_scan_kernel(IxParams p) {
   const uint8_t* kbase = (const uint8_t*)p.k + (int64_t)b * p.k_bs * C::ES;
   const float* ksc = (DT == DT_FP8) ? p.k_scale + (int64_t)b * p.ks_bs : nullptr;
   float* out = p.out + gi * (int64_t)p.n_k;
+  // B operands straight from HBM, one stage (64 keys) ahead of the MFMAs;
+  // rows past the end read key len-1 (masked on output).
+  typedef typename AFrag<DT>::T F;
+  auto load_stage = [&](int st, F (&bf)[2][C::NKS]) {
+    const int64_t s0 = slice0 + (int64_t)(wid + 4 * st) * kTileKeys;
+    const int64_t srow = s0 + (lane & 31);
+    const int64_t s_a = srow < len ? srow : len - 1;
+    const int64_t s_b = srow + 32 < len ? srow + 32 : len - 1;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      bf[0][ks] = load_frag<DT>(kbase + s_a * C::ROWB, ks, lane);
+      bf[1][ks] = load_frag<DT>(kbase + s_b * C::ROWB, ks, lane);
+    }
+  };
+  // prefetch only where the second set of operands fits the register budget
+  // (64 heads of bf16 d=128 would spill)
+  constexpr bool kPrefetch = 2 * C::NKS * sizeof(F) <= 128;
+  F cur[2][C::NKS], nxt[2][C::NKS];
+  if constexpr (kPrefetch) load_stage(0, cur);
 #pragma unroll 1
   for (int st = 0; st < kScanStagesPerWave; ++st) {
     const int64_t s0 = slice0 + (int64_t)(wid + 4 * st) * kTileKeys;
     if (s0 >= len) break;
-    // B operand straight from HBM; rows past the end read key len-1 (masked).
-    const int64_t srow = s0 + (lane & 31);
-    const int64_t s_a = srow < len ? srow : len - 1;
-    const int64_t s_b = srow + 32 < len ? srow + 32 : len - 1;
-    const uint8_t* base_a = kbase + s_a * C::ROWB;
-    const uint8_t* base_b = kbase + s_b * C::ROWB;
+    if constexpr (kPrefetch) {
+      if (st + 1 < kScanStagesPerWave && s0 + 4 * kTileKeys < len) load_stage(st + 1, nxt);
+    } else {
+      load_stage(st, cur);
+    }
     f32x16 acc[HT][2];
 #pragma unroll
     for (int h = 0; h < HT; ++h) { acc[h][0] = f32x16{}; acc[h][1] = f32x16{}; }
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) {
-      typename AFrag<DT>::T b0 = load_frag<DT>(base_a, ks, lane);
-      typename AFrag<DT>::T b1 = load_frag<DT>(base_b, ks, lane);
 #pragma unroll
       for (int h = 0; h < HT; ++h) {
-        acc[h][0] = mfma<DT>(rs.a[h][ks], b0, acc[h][0]);
-        acc[h][1] = mfma<DT>(rs.a[h][ks], b1, acc[h][1]);
+        acc[h][0] = mfma<DT>(rs.a[h][ks], cur[0][ks], acc[h][0]);
+        acc[h][1] = mfma<DT>(rs.a[h][ks], cur[1][ks], acc[h][1]);
       }
     }
     float p0 = 0.f, p1 = 0.f;
@@ -726,14 +749,17 @@ __global__ __launch_bounds__(256, 2) void ix_scan_kernel(IxParams p) {
         p1 = fmaf(rs.c[h][ii], fmaxf(acc[h][1][ii], 0.f), p1);
       }
     }
-    const bool lo = lane < 32;
-    const float send = lo ? p1 : p0;
-    const float recv = __shfl_xor(send, 32, 64);
-    float sc = (lo ? p0 : p1) + recv;
+    float sc = combine_halves(p0, p1);
     const int64_t s = s0 + lane;
     if (s < len) {
       if constexpr (DT == DT_FP8) sc *= ksc[s];
       out[s] = sc + 0.0f;
+    }
+    if constexpr (kPrefetch) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) cur[i][ks] = nxt[i][ks];
     }
   }
 }
@@ -877,8 +903,7 @@ hipError_t indexer_topk_fused(const dsa_indexer_args& a, int32_t k, int32_t* idx
   return hipErrorInvalidValue;
 }
 
-hipError_t indexer_scan(const dsa_indexer_args& a, float* scores, void* /*sel_ws*/, int32_t /*k*/,
-                        hipStream_t s) {
+hipError_t indexer_scan(const dsa_indexer_args& a, float* scores, hipStream_t s) {
   IxParams p = make_params(a);
   p.out = scores;
   if (a.dtype == DSA_BF16) {
