@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void indexer_f32_kernel(IxParams p, int dim, i
 }
 
 // ---------------------------------------------------------------- MFMA tiles
-template <int DT, int D>
+template <int DT, int D, int TK = kTileKeys>
 struct Cfg {
   static constexpr int ES = DT == DT_BF16 ? 2 : 1;          // element size
   static constexpr int ROWB = D * ES;                        // bytes per key row
@@ -90,11 +90,11 @@ struct Cfg {
   static constexpr int KSTEP = DT == DT_BF16 ? 16 : 64;      // MFMA K per instruction
   static constexpr int NKS = D / KSTEP;
   static constexpr int CPR = ROWB / 16;                      // 16-byte chunks per row
-  static constexpr int TILE_CHUNKS = kTileKeys * CPR;
+  static constexpr int TILE_CHUNKS = TK * CPR;
   static constexpr int NCH = TILE_CHUNKS / 256;              // chunks per thread
-  static constexpr int TILE_BYTES = kTileKeys * PITCH;
-  // staged tile of the fused kernel: the rows, then (fp8) the 64 key scales
-  static constexpr int BUF_BYTES = TILE_BYTES + (DT == DT_FP8 ? kTileKeys * 4 : 0);
+  static constexpr int TILE_BYTES = TK * PITCH;
+  // staged tile of the fused kernel: the rows, then (fp8) the TK key scales
+  static constexpr int BUF_BYTES = TILE_BYTES + (DT == DT_FP8 ? TK * 4 : 0);
 };
 
 template <int DT>
@@ -228,6 +228,46 @@ __device__ __forceinline__ float tile_scores(const RowState<DT, D, HT>& rs, cons
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
+// Scores of NG consecutive 64-key groups of an LDS tile (PITCH-byte rows):
+// sc[g] of lane l is key 64 g + l.  The 32-key subtiles run one after the
+// other, so each subtile's head-sum epilogue can overlap the next one's MFMAs
+// (only the last subtile's epilogue is left without MFMAs to hide under).
+template <int DT, int D, int HT, int NG>
+__device__ __forceinline__ void tile_scores_multi(const RowState<DT, D, HT>& rs, const uint8_t* kt, int lane,
+                                                  float (&sc)[NG]) {
+  typedef Cfg<DT, D> C;
+  float part[2 * NG];
+#pragma unroll
+  for (int n = 0; n < 2 * NG; ++n) {
+    f32x16 acc[HT];
+#pragma unroll
+    for (int h = 0; h < HT; ++h) acc[h] = f32x16{};
+    const uint8_t* rowp = kt + (32 * n + (lane & 31)) * C::PITCH;
+    typename AFrag<DT>::T bf = load_frag<DT>(rowp, 0, lane);
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      typename AFrag<DT>::T nxt = bf;
+      if (ks + 1 < C::NKS) nxt = load_frag<DT>(rowp, ks + 1, lane);
+#pragma unroll
+      for (int h = 0; h < HT; ++h) acc[h] = mfma<DT>(rs.a[h][ks], bf, acc[h]);
+      bf = nxt;
+    }
+    float pp = 0.f;
+#pragma unroll
+    for (int h = 0; h < HT; ++h) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pp = fmaf(rs.c[h][i], fmaxf(acc[h][i], 0.f), pp);
+    }
+    part[n] = pp;
+  }
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[2 * g]), __float_as_uint(part[2 * g + 1]),
+                                                     false, false);
+    sc[g] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+}
+
 // Half-wave combine of the two 32-key subtiles' partials (lanes l and l^32
 // hold complementary head rows of the same key column): lane l ends with key l.
 __device__ __forceinline__ float combine_halves(float p0, float p1) {
@@ -290,18 +330,20 @@ __device__ __forceinline__ void tile_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Direct HBM -> LDS staging of 64-key tiles (buffer_load ... lds).  Lane l of
-// one such load writes LDS bytes [base + 16 l, base + 16 l + 16), so a tile of
-// PITCH-byte rows (ROWB data bytes + 16 pad bytes) is SPR = CPR + 1 loads of 64
+// Direct HBM -> LDS staging of TK-key tiles (buffer_load ... lds).  Lane l of
+// one such load writes LDS bytes [base + 16 l, base + 16 l + 16), so 64 rows of
+// PITCH bytes (ROWB data bytes + 16 pad bytes) are SPR = CPR + 1 loads of 64
 // 16-byte slots: slot q holds part q % SPR of row q / SPR, and pad slots read
 // past the buffer's end (zeros).  Load j of a tile is issued by wave j % W.
 // Offsets go in the per-lane offset so that the buffer's range check covers
 // them: keys at or past the end of the range read as zero.
-template <int DT, int D, int W>
+template <int DT, int D, int W, int TK>
 struct TileDma {
-  typedef Cfg<DT, D> C;
+  typedef Cfg<DT, D, TK> C;
   static constexpr int SPR = C::CPR + 1;
-  static constexpr int NI = SPR + (DT == DT_FP8 ? 1 : 0);   // + one 4-byte-per-lane load of the key scales
+  static constexpr int NG = TK / 64;                       // 64-row groups per tile
+  static constexpr int NR = NG * SPR;                      // loads of rows and pads
+  static constexpr int NI = NR + (DT == DT_FP8 ? NG : 0);  // + 4-byte-per-lane loads of the key scales
   static constexpr int NPW = (NI + W - 1) / W;       // loads per wave and tile, at most (W waves)
   uint32_t goff[NPW];
   int nload;                                          // loads this wave issues per tile
@@ -318,14 +360,15 @@ struct TileDma {
   // sr: the key scales (fp8), as a buffer of floats
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, __amdgpu_buffer_rsrc_t sr, int tile,
                                        uint8_t* dst, int lane) const {
-    const uint32_t toff = (uint32_t)tile * (kTileKeys * C::ROWB);
+    const uint32_t toff = (uint32_t)tile * (TK * C::ROWB);
 #pragma unroll
     for (int m = 0; m < NPW; ++m) {
       const int j = wid + W * m;
-      if (j < SPR) {
+      if (j < NR) {
         lds_dma<16>(r, dst + j * 1024, goff[m] + toff);
-      } else if (DT == DT_FP8 && j == SPR) {
-        lds_dma<4>(sr, dst + C::TILE_BYTES, (uint32_t)(tile * kTileKeys + lane) * 4u);
+      } else if (DT == DT_FP8 && j < NI) {
+        const int g = j - NR;
+        lds_dma<4>(sr, dst + C::TILE_BYTES + 256 * g, (uint32_t)(tile * TK + 64 * g + lane) * 4u);
       }
     }
   }
@@ -351,7 +394,6 @@ struct TileDma {
 __device__ __forceinline__ void lds_sync() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup"); }
 
 constexpr int kCandCap = 16384;        // candidates per row before a compaction
-constexpr int kTileStages = 3;         // LDS tile buffers of the fused kernel (prefetch depth + 1)
 
 // Entries [j, j+4) of a candidate array in one 16-byte load.  The arrays are
 // 16-byte aligned and their capacity is a multiple of 4, so a load that starts
@@ -577,9 +619,15 @@ __global__ __launch_bounds__(256, 2) void ix_scores_kernel(IxParams p) {
 template <int DT, int D, int HT>
 __global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk_kernel(IxParams p, uint32_t* work,
                                                                                     uint32_t* cand) {
-  typedef Cfg<DT, D> C;
-  // staging buffers: tiles it+1 .. it+kTileStages-1 load while tile it is scored
-  __shared__ __attribute__((aligned(16))) uint8_t ktile[kTileStages][C::BUF_BYTES];
+  // 128-key tiles where two buffers of three fit two workgroups per CU in LDS
+  // (fp8 and the narrower bf16 rows); 64-key tiles for bf16 d = 128
+  constexpr int TK = Cfg<DT, D, 128>::BUF_BYTES <= 24576 ? 128 : 64;
+  constexpr int NG = TK / 64;
+  typedef Cfg<DT, D, TK> C;
+  // staging buffers (as many as fit two workgroups per CU, at most 3): tiles
+  // it+1 .. it+STAGES-1 load while tile it is scored
+  constexpr int STAGES = C::BUF_BYTES > 24576 ? 2 : 3;
+  __shared__ __attribute__((aligned(16))) uint8_t ktile[STAGES][C::BUF_BYTES];
   __shared__ uint32_t hist[kTopkWaves][256];
   __shared__ int64_t s_item;
 
@@ -592,7 +640,7 @@ __global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk_kernel
   const int64_t nrb = (p.rows + kTopkWaves - 1) / kTopkWaves;
   const int64_t total = nrb * p.batch;
   const int k = p.topk;
-  const TileDma<DT, D, kTopkWaves> td(wid, lane);
+  const TileDma<DT, D, kTopkWaves, TK> td(wid, lane);
 
   for (;;) {
     if (threadIdx.x == 0) s_item = (int64_t)atomicAdd(work, 1u);
@@ -611,7 +659,7 @@ __global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk_kernel
     const int64_t rlast = rloc0 + kTopkWaves - 1 < p.rows ? rloc0 + kTopkWaves - 1 : p.rows - 1;
     const int64_t t_last = p.q_pos0 + p.row0 + rlast;
     const int nkeys = (int)(t_last + 1 < p.n_k ? t_last + 1 : p.n_k);
-    const int ntiles = (nkeys + kTileKeys - 1) / kTileKeys;
+    const int ntiles = (nkeys + TK - 1) / TK;
     const int tlim = t < p.n_k - 1 ? t : p.n_k - 1;             // last candidate position
     const int64_t gi = (int64_t)b * p.n_q + i;
 
@@ -629,37 +677,42 @@ __global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk_kernel
     bool full = false, strict = false;
     uint32_t thr = 0;
 #pragma unroll
-    for (int i = 0; i < kTileStages - 1; ++i)
+    for (int i = 0; i < STAGES - 1; ++i)
       if (i < ntiles) td.load(krs, srs, i, ktile[i], lane);
     for (int it = 0; it < ntiles; ++it) {
       // tiles it .. it+younger are in flight; this wave's loads of tile it must be done
       const int ahead = ntiles - 1 - it;
-      td.wait_oldest(ahead < kTileStages - 2 ? ahead : kTileStages - 2);
+      td.wait_oldest(ahead < STAGES - 2 ? ahead : STAGES - 2);
       tile_barrier();
-      // buffer (it-1) % kTileStages was last read in iteration it-1, which every wave has left
-      if (it + kTileStages - 1 < ntiles)
-        td.load(krs, srs, it + kTileStages - 1, ktile[(it + kTileStages - 1) % kTileStages], lane);
-      const uint8_t* kt = ktile[it % kTileStages];
-      const int s0 = it * kTileKeys;
-      if (s0 <= tlim) {
-        float sc = tile_scores<DT, D, HT>(rs, kt, C::PITCH, lane);
-        const int s = s0 + lane;
-        if constexpr (DT == DT_FP8) sc *= *(const float*)(kt + C::TILE_BYTES + lane * 4);
-        const uint32_t u = order_key(sc);
-        if (cnt + 64 > kCandCap) {
-          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-          cnt = wave_shrink(cu, ci, cnt, k, hist[wid], lane, thr, strict);
-          full = true;
-          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+      // buffer (it-1) % STAGES was last read in iteration it-1, which every wave has left
+      if (it + STAGES - 1 < ntiles) td.load(krs, srs, it + STAGES - 1, ktile[(it + STAGES - 1) % STAGES], lane);
+      const uint8_t* kt = ktile[it % STAGES];
+      if (it * TK <= tlim) {
+        float sc[NG];
+        tile_scores_multi<DT, D, HT, NG>(rs, kt, lane, sc);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          const int s0 = it * TK + 64 * g;
+          if (s0 > tlim) break;
+          const int s = s0 + lane;
+          float v = sc[g];
+          if constexpr (DT == DT_FP8) v *= *(const float*)(kt + C::TILE_BYTES + (64 * g + lane) * 4);
+          const uint32_t u = order_key(v);
+          if (cnt + 64 > kCandCap) {
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+            cnt = wave_shrink(cu, ci, cnt, k, hist[wid], lane, thr, strict);
+            full = true;
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+          }
+          const bool pr = s <= tlim && (!full || (strict ? u > thr : u >= thr));
+          const uint64_t m = ballot(pr);
+          if (pr) {
+            const uint32_t d = (uint32_t)cnt + lanes_below(m);
+            __builtin_amdgcn_raw_buffer_store_b32(u, crs, d * 4u, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32((uint32_t)s, crs, d * 4u, kCandCap * 4, 0);
+          }
+          cnt += __builtin_popcountll(m);
         }
-        const bool pr = s <= tlim && (!full || (strict ? u > thr : u >= thr));
-        const uint64_t m = ballot(pr);
-        if (pr) {
-          const uint32_t d = (uint32_t)cnt + lanes_below(m);
-          __builtin_amdgcn_raw_buffer_store_b32(u, crs, d * 4u, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b32((uint32_t)s, crs, d * 4u, kCandCap * 4, 0);
-        }
-        cnt += __builtin_popcountll(m);
       }
     }
     if (vrow) {
