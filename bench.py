@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-report", action="store_true", help="skip the all-F comparison and overlap matrix")
+    p.add_argument("--sweep", action="store_true",
+                   help="retention sweep instead of the bench line: both stacks under all-F, uniform 1/2, 1/4, "
+                        "1/8 and (decode) the searched 47-layer patterns; prints one JSON object")
     p.add_argument("--profile", choices=["indexer", "copy"], default=None,
                    help="counter-collection runs: 'indexer' launches only the prefill F layer's fused "
                         "indexer+Top-k (3 launches, the first a warm-up); 'copy' runs a 1 GiB read + "
@@ -179,6 +182,92 @@ def profile_run(args, dev):
         print(f"profile indexer: fused indexer+Top-k L={L} launch {i + 1}/3 done", flush=True)
 
 
+def sweep_run(args, dev):
+    """Stack time per sharing pattern (same kernels and driver as the bench line)."""
+    import dsa_lightning_indexer_amd as dsa
+    from synth import inputs as syn
+    topk = 2048
+    res = {"metric": "stack time per sharing pattern (retention sweep)", "unit": "ms", "data": "synthetic"}
+
+    def run(pattern, specs, reps):
+        ws = torch.empty(max(dsa.indexcache_forward_workspace_size(pattern, specs, topk), 256),
+                         dtype=torch.uint8, device=dev)
+        dsa.indexcache_forward(pattern, specs, topk, ws=ws)
+        torch.cuda.synchronize()
+        t = time_launches(lambda: dsa.indexcache_forward(pattern, specs, topk, ws=ws), reps)
+        return sum(t) / len(t)
+
+    # decode stack: every layer has attention inputs; indexer inputs for any layer a pattern makes F
+    B, S, NL = args.decode_batch, args.decode_len, args.decode_layers
+    sa = [syn.c5_layer_sa(l, B=B, S=S, device=dev) for l in range(NL)]
+    ix = [syn.c5_layer_indexer(l, B=B, S=S, device=dev) for l in range(NL)]
+    outs = [torch.empty((B, 1, 16, 512), dtype=torch.float32, device=dev) for _ in range(NL)]
+    idxs = [torch.empty((B, 1, topk), dtype=torch.int32, device=dev) for _ in range(NL)]
+    torch.cuda.synchronize()
+    log("sweep: decode inputs ready")
+
+    def dspecs(pattern):
+        specs = []
+        for l, c in enumerate(pattern):
+            spec = {"sa": {"q": sa[l].q, "kv": sa[l].kv, "scale": sa[l].scale, "d_v": 512, "out": outs[l]}}
+            if c == "F":
+                x = ix[l]
+                spec["ix"] = {"q": x.q, "k": x.k, "w": x.w, "q_scale": x.q_scale, "k_scale": x.k_scale,
+                              "q_pos0": x.q_pos0}
+                spec["idx_out"] = idxs[l]
+            specs.append(spec)
+        return specs
+
+    pats = [("all-F", "F" * NL)]
+    for r, name in ((2, "1/2"), (4, "1/4"), (8, "1/8")):
+        pats.append((f"uniform {name}", syn.uniform_pattern(NL, r)))
+        if NL == 47:
+            pats.append((f"searched {name}", syn.SEARCHED_PATTERNS_47[name]))
+    rows = []
+    for name, pat in pats:
+        ms = run(pat, dspecs(pat), 5)
+        rows.append({"pattern": name, "F_layers": pat.count("F"), "ms": ms})
+        log(f"sweep decode {name:13s} F={pat.count('F'):2d}: {ms:.3f} ms")
+    base = rows[0]["ms"]
+    for r in rows:
+        r["speedup_vs_all_F"] = base / r["ms"]
+    res["decode"] = {"workload": f"decode stack B={B} x S={S} x {NL} layers, fp8 indexer K cache, k={topk}",
+                     "rows": rows}
+    del sa, ix, outs, idxs
+    torch.cuda.empty_cache()
+
+    # prefill stack
+    L = args.prefill_len
+    layers = syn.c4_stack(L=L, n_layers=8, seed=4, device=dev)
+    pouts = [torch.empty((1, L, 16, 512), dtype=torch.float32, device=dev) for _ in range(8)]
+    pidx = [torch.empty((1, L, topk), dtype=torch.int32, device=dev) for _ in range(8)]
+    torch.cuda.synchronize()
+    log("sweep: prefill inputs ready")
+
+    def pspecs(pattern):
+        specs = []
+        for l, c in enumerate(pattern):
+            x, a = layers[l]
+            spec = {"sa": {"q": a.q, "kv": a.kv, "scale": a.scale, "d_v": 512, "out": pouts[l]}}
+            if c == "F":
+                spec["ix"] = {"q": x.q, "k": x.k, "w": x.w}
+                spec["idx_out"] = pidx[l]
+            specs.append(spec)
+        return specs
+
+    rows = []
+    for name, pat in (("all-F", "FFFFFFFF"), ("uniform 1/2", "FSFSFSFS"), ("uniform 1/4", "FSSSFSSS"),
+                      ("uniform 1/8", "FSSSSSSS")):
+        ms = run(pat, pspecs(pat), 2)
+        rows.append({"pattern": name, "F_layers": pat.count("F"), "ms": ms})
+        log(f"sweep prefill {name:13s} F={pat.count('F')}: {ms:.1f} ms")
+    base = rows[0]["ms"]
+    for r in rows:
+        r["speedup_vs_all_F"] = base / r["ms"]
+    res["prefill"] = {"workload": f"prefill stack L={L} x 8 layers, bf16 indexer, k={topk}", "rows": rows}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -189,6 +278,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.profile:
         profile_run(args, dev)
+        return
+    if args.sweep:
+        sweep_run(args, dev)
         return
     import dsa_lightning_indexer_amd as dsa
     from synth import inputs as syn

@@ -28,7 +28,7 @@ __all__ = [
     "F32", "BF16", "FP8", "IndexerInputs", "SAInputs", "generator",
     "fp8_encode_vectors", "indexer_inputs", "sa_inputs", "random_sorted_indices",
     "c4_stack", "c5_layer_indexer", "c5_layer_sa", "CONFIGS", "C5_PATTERN",
-    "uniform_pattern",
+    "uniform_pattern", "SEARCHED_PATTERNS_47",
 ]
 
 
@@ -171,6 +171,17 @@ def uniform_pattern(n_layers: int, r: int) -> str:
 
 
 C5_PATTERN = uniform_pattern(47, 4)   # F at layers 1,5,...,45 (1-based): 12 F layers
+
+# Greedy-searched sharing patterns of the 47-layer GLM-4.7-Flash 30B DSA model at
+# retention 1/2, 1/4 and 1/8 ([DSA-NOTES] Appendix B, "搜索到的模式"): data for the
+# pattern driver (layer l is F or S), not method arithmetic.  The 1/8 string is
+# printed with 48 characters for the 47 layers; its trailing S is dropped (every
+# printed F position is kept).
+SEARCHED_PATTERNS_47 = {
+    "1/2": "FSFSFSSSSFSFFFFSFFSSFFSFFFSSFFSSFSSSSFSFFFSFSSF",
+    "1/4": "FSFSFSSSSFSSSFSSFFSSFSSFSSSSFSSSFSSSSFSSSSSSSSS",
+    "1/8": "FSSSFSSSSSSSSFSSSFSSSSSFSSSSFSSSSSSSSSFSSSSSSSSS"[:47],
+}
 
 
 # --- named workloads ---------------------------------------------------------

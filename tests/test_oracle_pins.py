@@ -318,6 +318,27 @@ def test_pattern_rules():
     assert [i + 1 for i, c in enumerate(syn.C5_PATTERN) if c == "F"] == list(range(1, 46, 4))
 
 
+def test_searched_patterns_from_the_page():
+    """[DSA-NOTES] Appendix B: the searched 47-layer patterns keep 24, 12 and 7 F
+    layers; the driver inputs match the printed strings (the 1/8 one with its
+    extra trailing S dropped) and every one starts with an F layer."""
+    g = gold("searched_patterns.json")
+    for r, text in g["patterns_as_printed"].items():
+        used = syn.SEARCHED_PATTERNS_47[r]
+        assert len(used) == g["n_layers"]
+        assert used == text[:g["n_layers"]]
+        assert text[g["n_layers"]:] in ("", "S")
+        assert used.count("F") == text.count("F") == g["f_counts"][r]
+        src = oracle.source_layers(used)
+        assert src[0] == 1 and None not in src
+        # an S layer's source is the nearest F layer before it
+        for l, c in enumerate(used, start=1):
+            if c == "F":
+                assert src[l - 1] == l
+            else:
+                assert used[src[l - 1] - 1] == "F" and "F" not in used[src[l - 1]:l - 1]
+
+
 # --- overlap and report arithmetic ---------------------------------------------------------
 
 def test_overlap_worked_example():
