@@ -88,12 +88,13 @@ TopkPath topk_path(const dsa_indexer_args* a, const float* scores) {
 
 size_t topk_ws(const dsa_indexer_args* a, const float* scores) {
   const int64_t rows = (int64_t)a->batch * a->n_q;
+  const size_t sel = rows <= dsa_host::kSelectFewRows ? dsa_host::select_few_ws_bytes(rows)
+                                                       : dsa_host::select_workspace_bytes(rows);
   switch (topk_path(a, scores)) {
-    case PATH_SELECT: return align_up(dsa_host::select_workspace_bytes(rows));
+    case PATH_SELECT: return align_up(sel);
     case PATH_F32:
     case PATH_SCAN:
-      return align_up((size_t)rows * a->n_k * sizeof(float)) +
-             align_up(dsa_host::select_workspace_bytes(rows));
+      return align_up((size_t)rows * a->n_k * sizeof(float)) + align_up(sel);
     case PATH_FUSED: return align_up(dsa_host::topk_fused_ws_bytes());
   }
   return 0;
@@ -147,9 +148,13 @@ dsa_status run_topk(const dsa_indexer_args* a, const float* scores, int32_t k, i
     if (e != hipSuccess) return hip_status(e, "indexer scoring launch");
     sc = buf;
   }
-  e = dsa_host::select_prepare(sel_ws, rows, s);
-  if (e == hipSuccess) e = dsa_host::select_hist1(sc, plan, sel_ws, s);
-  if (e == hipSuccess) e = dsa_host::select_finish(sc, plan, sel_ws, idx, s);
+  if (rows <= dsa_host::kSelectFewRows) {
+    e = dsa_host::select_few(sc, plan, sel_ws, idx, s);
+  } else {
+    e = dsa_host::select_prepare(sel_ws, rows, s);
+    if (e == hipSuccess) e = dsa_host::select_hist1(sc, plan, sel_ws, s);
+    if (e == hipSuccess) e = dsa_host::select_finish(sc, plan, sel_ws, idx, s);
+  }
   return hip_status(e, "top-k select launch");
 }
 

@@ -97,6 +97,12 @@ hipError_t select_hist1(const float* scores, const SelectPlan& p, void* ws, hipS
 hipError_t select_finish(const float* scores, const SelectPlan& p, void* ws, int32_t* idx,
                          hipStream_t s);
 
+// Few long rows (at most kSelectFewRows): sample threshold, candidate collection
+// and an exact select over the candidates (select_few.hip).
+constexpr int64_t kSelectFewRows = 256;
+size_t select_few_ws_bytes(int64_t rows);
+hipError_t select_few(const float* scores, const SelectPlan& p, void* ws, int32_t* idx, hipStream_t s);
+
 hipError_t indexer_scores_f32(const dsa_indexer_args& a, int64_t row0, int64_t rows, float* out,
                               int64_t out_row_stride, hipStream_t s);
 hipError_t indexer_scores_mfma(const dsa_indexer_args& a, int64_t row0, int64_t rows, float* out,

@@ -312,14 +312,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // the compiler's wait-count tracking, which would otherwise wait for the load
 // before every later LDS read of the same array, leaves it alone; callers wait
 // for it explicitly (vmcnt) before the barrier that publishes the data.  The
-// asm has no register outputs.
+// load takes its LDS base from M0, which the compiler reserves: the asm saves
+// M0, sets it (one wait state before the load reads it) and restores it.  Its
+// only register output is that saved copy.
 template <int BYTES>
 __device__ __forceinline__ void lds_dma(__amdgpu_buffer_rsrc_t r, const uint8_t* lds, uint32_t voff) {
   const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)lds;
+  uint32_t saved;
   if constexpr (BYTES == 16)
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(a), "v"(voff), "s"(r) : "memory", "m0");
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(a), "v"(voff), "s"(r) : "memory");
   else
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(a), "v"(voff), "s"(r) : "memory", "m0");
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %2, %3, 0 offen lds\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(a), "v"(voff), "s"(r) : "memory");
 }
 
 // Workgroup barrier without the fence of __syncthreads (whose release would

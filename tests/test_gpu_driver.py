@@ -120,3 +120,36 @@ def test_decode_stack_fsss(dsa, dev):
             ref = oracle.sparse_attn(Q, K, V, T, sas[l].scale)
             got = specs[l]["sa"]["out"][b].cpu().numpy()
             assert H.attn_close(got, ref) <= H.ATTN_RTOL
+
+
+@pytest.mark.parametrize("retention", ["1/4", "1/8"])
+def test_searched_47_layer_pattern_on_gpu(dsa, dev, retention):
+    """A searched 47-layer sharing pattern ([DSA-NOTES] Appendix B) through the
+    driver: every F layer's index tensor is bit-exact against the oracle on
+    integer inputs, every layer attends with the tensor of its source layer
+    (compared on sampled rows), and no S layer gets indexer inputs."""
+    pattern = syn.SEARCHED_PATTERNS_47[retention]
+    L, topk = 320, 64
+    layers, specs = build_stack(dev, pattern, L, topk)
+    src = dsa.indexcache_forward(pattern, specs, topk)
+    torch.cuda.synchronize()
+    assert [s + 1 for s in src] == oracle.source_layers(pattern)
+
+    def indexer_fn(l):
+        ix = layers[l - 1][0]
+        q, k, w = H.indexer_f64(ix)
+        return oracle.indexer_topk(q, k, w, topk)[0]
+
+    rows = np.array([0, 63, 64, 200, L - 1])
+
+    def attn_fn(l, T):
+        Q, K, V = H.sa_f64(layers[l - 1][1])
+        return oracle.sparse_attn(Q, K, V, T, layers[l - 1][1].scale, rows=rows)
+
+    osrc, Ts, outs, calls = oracle.indexcache_forward(pattern, indexer_fn, attn_fn)
+    assert calls == [l + 1 for l, c in enumerate(pattern) if c == "F"]
+    for l in range(len(pattern)):
+        if pattern[l] == "F":
+            assert np.array_equal(specs[l]["idx_out"][0].cpu().numpy(), Ts[l]), f"layer {l + 1} index"
+        got = specs[l]["sa"]["out"][0].cpu().numpy()[rows]
+        assert H.attn_close(got, outs[l]) <= H.ATTN_RTOL, f"layer {l + 1} attention"

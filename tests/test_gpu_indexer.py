@@ -162,6 +162,28 @@ def test_select_from_given_scores_with_ties(dsa, dev):
             assert np.array_equal(got[b, i], ref), (b, i)
 
 
+def test_select_few_rows_threshold_and_fallbacks(dsa, dev):
+    """Few long rows go through the sampled-threshold select.  Row 0: ordinary
+    float scores (candidate path).  Row 1: the sampled positions (every 25th)
+    hold a few very high scores, so fewer than k keys reach the sample's
+    threshold and the whole-row select runs.  Row 2: all scores equal, so every
+    key reaches the threshold (more than the candidate buffer holds): whole-row
+    select again, ties broken by position.  Exact against the oracle."""
+    g = torch.Generator(device=dev).manual_seed(13)
+    n_k, topk = 204800, 2048
+    sc = torch.randn((3, 1, n_k), generator=g, device=dev)
+    stride = (n_k + 8191) // 8192
+    sc[1, 0, torch.arange(200, device=dev) * stride] = 100.0 + torch.arange(200, device=dev).float()
+    sc[2, 0] = 0.5
+    dummy_q = torch.zeros((3, 1, 1, 32), dtype=torch.bfloat16, device=dev)
+    dummy_k = torch.zeros((3, n_k, 32), dtype=torch.bfloat16, device=dev)
+    dummy_w = torch.zeros((3, 1, 1), device=dev)
+    got = dsa.topk(dummy_q, dummy_k, dummy_w, topk, q_pos0=n_k - 1, scores=sc).cpu().numpy()
+    s64 = sc.cpu().double().numpy()
+    for b in range(3):
+        assert np.array_equal(got[b, 0], oracle.topk_row(s64[b, 0], topk)), b
+
+
 # --------------------------------------------------------------------------- decode scan
 @pytest.mark.parametrize("dtype", [syn.FP8, syn.BF16])
 def test_decode_scan_integer_exact_and_matches_prefill_row(dsa, dev, dtype):
