@@ -52,6 +52,7 @@ struct IxParams {
   float* out;            // scores [batch, rows, n_k]
   int32_t* idx;          // [batch, n_q, topk]
   int32_t topk;
+  int64_t scan_slice;    // decode scan: keys per workgroup (a multiple of 256)
 };
 
 // ---------------------------------------------------------------- fp32 path
@@ -742,8 +743,9 @@ __global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk_kernel
 }
 
 // ---------------------------------------------------------------- decode scan
-constexpr int kScanStagesPerWave = 8;  // 64 keys each
-constexpr int kScanSlice = kTileKeys * kScanStagesPerWave * 4;
+// The grid holds about two workgroups per CU (one round, no tail); workgroup
+// (slice, row) scores keys [slice * scan_slice, (slice + 1) * scan_slice) of its
+// row, its wave w taking the 64-key stages w, w + 4, w + 8, ...
 
 template <int DT, int D, int HT>
 __global__ __launch_bounds__(256, 2) void ix_scan_kernel(IxParams p) {
@@ -754,8 +756,10 @@ __global__ __launch_bounds__(256, 2) void ix_scan_kernel(IxParams p) {
   const int64_t i = gi % p.n_q;
   const int64_t t = p.q_pos0 + i;
   const int64_t len = t + 1 < p.n_k ? t + 1 : p.n_k;
-  const int64_t slice0 = (int64_t)blockIdx.x * kScanSlice;
+  const int64_t slice0 = (int64_t)blockIdx.x * p.scan_slice;
   if (slice0 >= len) return;
+  const int64_t slice1 = slice0 + p.scan_slice < len ? slice0 + p.scan_slice : len;
+  const int nstages = (int)((slice1 - slice0 + 4 * kTileKeys - 1) / (4 * kTileKeys));
   RowState<DT, D, HT> rs;
   load_row<DT, D, HT>(p, gi, lane, rs);
   const uint8_t* kbase = (const uint8_t*)p.k + (int64_t)b * p.k_bs * C::ES;
@@ -781,11 +785,11 @@ __global__ __launch_bounds__(256, 2) void ix_scan_kernel(IxParams p) {
   F cur[2][C::NKS], nxt[2][C::NKS];
   if constexpr (kPrefetch) load_stage(0, cur);
 #pragma unroll 1
-  for (int st = 0; st < kScanStagesPerWave; ++st) {
+  for (int st = 0; st < nstages; ++st) {
     const int64_t s0 = slice0 + (int64_t)(wid + 4 * st) * kTileKeys;
-    if (s0 >= len) break;
+    if (s0 >= slice1) break;
     if constexpr (kPrefetch) {
-      if (st + 1 < kScanStagesPerWave && s0 + 4 * kTileKeys < len) load_stage(st + 1, nxt);
+      if (st + 1 < nstages && s0 + 4 * kTileKeys < slice1) load_stage(st + 1, nxt);
     } else {
       load_stage(st, cur);
     }
@@ -811,7 +815,7 @@ __global__ __launch_bounds__(256, 2) void ix_scan_kernel(IxParams p) {
     }
     float sc = combine_halves(p0, p1);
     const int64_t s = s0 + lane;
-    if (s < len) {
+    if (s < slice1) {
       if constexpr (DT == DT_FP8) sc *= ksc[s];
       out[s] = sc + 0.0f;
     }
@@ -893,9 +897,15 @@ hipError_t launch_topk_dt(const IxParams& p, void* ws, hipStream_t s) {
 }
 
 template <int DT, int D>
-hipError_t launch_scan_dt(const IxParams& p, hipStream_t s) {
+hipError_t launch_scan_dt(const IxParams& p0, hipStream_t s) {
+  IxParams p = p0;
   const int64_t len = p.q_pos0 + p.n_q < p.n_k ? p.q_pos0 + p.n_q : p.n_k;
-  dim3 grid((unsigned)((len + kScanSlice - 1) / kScanSlice), (unsigned)((int64_t)p.batch * p.n_q));
+  const int64_t rows = (int64_t)p.batch * p.n_q;
+  // about two workgroups per CU over all rows, slices of whole 256-key groups
+  int64_t per_row = (persistent_blocks() + rows - 1) / rows;
+  if (per_row < 1) per_row = 1;
+  p.scan_slice = ((len + per_row - 1) / per_row + 255) / 256 * 256;
+  dim3 grid((unsigned)((len + p.scan_slice - 1) / p.scan_slice), (unsigned)rows);
   if (p.heads > 32) {
     hipLaunchKernelGGL((ix_scan_kernel<DT, D, 2>), grid, dim3(256), 0, s, p);
   } else {
