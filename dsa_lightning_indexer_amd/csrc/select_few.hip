@@ -140,9 +140,20 @@ __global__ __launch_bounds__(kThreads) void tau_kernel(const float* __restrict__
     return;
   }
   const float* row = scores + r * row_stride;
-  const int64_t stride = (len + kSampleMax - 1) / kSampleMax;
-  const int ns = (int)((len + stride - 1) / stride);
-  for (int i = threadIdx.x; i < ns; i += kThreads) skey[i] = dsa::order_key(row[(int64_t)i * stride]);
+  // the sample: kRuns runs of kRunLen consecutive scores spread evenly over the
+  // row (whole 64-byte pieces instead of one score per cache line)
+  constexpr int kRunLen = 16, kRuns = kSampleMax / kRunLen;
+  const int64_t gap = (len - kRunLen) / (kRuns - 1);        // >= kRunLen since len > kCandMax
+  const int ns = kSampleMax;
+  {
+    const int run = (int)threadIdx.x >> 1, half = (int)threadIdx.x & 1;   // 2 threads per run, 8 scores each
+    const float* src = row + (int64_t)run * gap + 8 * half;
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = src[j];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) skey[run * kRunLen + 8 * half + j] = dsa::order_key(v[j]);
+  }
   __syncthreads();
   // rank in the sample of a key that about 2k keys of the row reach
   int64_t m = (2 * (int64_t)k * ns + len - 1) / len;
@@ -304,9 +315,24 @@ __global__ __launch_bounds__(kThreads) void final_kernel(const float* __restrict
     return;
   }
   const int n = (int)total;
-  for (int i = threadIdx.x; i < n; i += kThreads) {
-    ckey[i] = ld_agent(&rw[kKeys + i]);
-    cpos[i] = ld_agent(&rw[kPos + i]);
+  {
+    // candidates written by the previous kernel: plain loads, all in flight at once
+    constexpr int PER = kCandMax / kThreads;
+    uint32_t kk[PER], pp[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = (int)threadIdx.x + j * kThreads;
+      kk[j] = i < n ? rw[kKeys + i] : 0u;
+      pp[j] = i < n ? rw[kPos + i] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = (int)threadIdx.x + j * kThreads;
+      if (i < n) {
+        ckey[i] = kk[j];
+        cpos[i] = pp[j];
+      }
+    }
   }
   __syncthreads();
   uint32_t T, req;

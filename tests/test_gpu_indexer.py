@@ -164,16 +164,18 @@ def test_select_from_given_scores_with_ties(dsa, dev):
 
 def test_select_few_rows_threshold_and_fallbacks(dsa, dev):
     """Few long rows go through the sampled-threshold select.  Row 0: ordinary
-    float scores (candidate path).  Row 1: the sampled positions (every 25th)
-    hold a few very high scores, so fewer than k keys reach the sample's
-    threshold and the whole-row select runs.  Row 2: all scores equal, so every
-    key reaches the threshold (more than the candidate buffer holds): whole-row
+    float scores (candidate path).  Row 1: the first 200 of the sampler's 512
+    runs of 16 positions (spread evenly: run j starts at j * (n - 16) // 511)
+    hold very high scores, so fewer than k keys reach the sample's threshold
+    and the whole-row select runs.  Row 2: all scores equal, so every key
+    reaches the threshold (more than the candidate buffer holds): whole-row
     select again, ties broken by position.  Exact against the oracle."""
     g = torch.Generator(device=dev).manual_seed(13)
     n_k, topk = 204800, 2048
     sc = torch.randn((3, 1, n_k), generator=g, device=dev)
-    stride = (n_k + 8191) // 8192
-    sc[1, 0, torch.arange(200, device=dev) * stride] = 100.0 + torch.arange(200, device=dev).float()
+    gap = (n_k - 16) // 511
+    pos = (torch.arange(200, device=dev).view(-1, 1) * gap + torch.arange(16, device=dev).view(1, -1)).flatten()
+    sc[1, 0, pos] = 100.0 + torch.arange(pos.numel(), device=dev).float()
     sc[2, 0] = 0.5
     dummy_q = torch.zeros((3, 1, 1, 32), dtype=torch.bfloat16, device=dev)
     dummy_k = torch.zeros((3, n_k, 32), dtype=torch.bfloat16, device=dev)
