@@ -325,6 +325,14 @@ def main():
     # phase times (same calls, events per phase)
     ms_prefill = sum(time_launches(lambda: dsa.indexcache_forward(pattern_p, pspecs, topk, ws=ws_p), 2)) / 2
     ms_decode = sum(time_launches(lambda: dsa.indexcache_forward(pattern_d, dspecs, topk, ws=ws_d), 3)) / 3
+    # the same decode layer loop captured once in a HIP graph and replayed
+    dgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(dgraph):
+        dsa.indexcache_forward(pattern_d, dspecs, topk, ws=ws_d)
+    dgraph.replay()
+    torch.cuda.synchronize()
+    ms_decode_graph = sum(time_launches(dgraph.replay, 5)) / 5
+    log(f"decode stack: {ms_decode:.3f} ms eager, {ms_decode_graph:.3f} ms as a HIP graph")
 
     # dominant kernel: the fused indexer+Top-k launch of an F prefill layer
     ix0 = players[0][0]
@@ -376,6 +384,7 @@ def main():
         "phases": {
             "prefill_stack_ms": ms_prefill,
             "decode_stack_ms": ms_decode,
+            "decode_stack_graph_ms": ms_decode_graph,
             "decode_tokens_per_s": B / (ms_decode * 1e-3),
             "prefill_indexer_topk_ms_per_F_layer": k_ms,
             "decode_indexer_topk_ms_per_F_layer": d_ms,

@@ -137,19 +137,27 @@ dsa_status run_topk(const dsa_indexer_args* a, const float* scores, int32_t k, i
   }
   const float* sc = scores;
   void* sel_ws = ws;
+  const bool few = rows <= dsa_host::kSelectFewRows;
   if (path == PATH_F32 || path == PATH_SCAN) {
     float* buf = (float*)ws;
     sel_ws = (char*)ws + align_up((size_t)rows * a->n_k * sizeof(float));
-    if (path == PATH_F32) {
-      e = dsa_host::indexer_scores_f32(*a, 0, a->n_q, buf, a->n_k, s);
-    } else {
-      e = dsa_host::indexer_scan(*a, buf, s);
-    }
-    if (e != hipSuccess) return hip_status(e, "indexer scoring launch");
     sc = buf;
   }
-  if (rows <= dsa_host::kSelectFewRows) {
-    e = dsa_host::select_few(sc, plan, sel_ws, idx, s);
+  if (few) {
+    e = dsa_host::select_few_prepare(sel_ws, rows, s);
+    if (e != hipSuccess) return hip_status(e, "top-k select launch");
+  }
+  if (path == PATH_F32) {
+    e = dsa_host::indexer_scores_f32(*a, 0, a->n_q, (float*)sc, a->n_k, s);
+  } else if (path == PATH_SCAN) {
+    // the scan builds the few-row select's key histograms as it writes the scores
+    const dsa_host::FewHist h = dsa_host::select_few_hist(sel_ws);
+    e = dsa_host::indexer_scan(*a, (float*)sc, few ? &h : nullptr, s);
+  }
+  if (e != hipSuccess) return hip_status(e, "indexer scoring launch");
+  if (few) {
+    if (path != PATH_SCAN) e = dsa_host::select_few_hist_scores(sc, plan, sel_ws, s);
+    if (e == hipSuccess) e = dsa_host::select_few_finish(sc, plan, sel_ws, idx, s);
   } else {
     e = dsa_host::select_prepare(sel_ws, rows, s);
     if (e == hipSuccess) e = dsa_host::select_hist1(sc, plan, sel_ws, s);

@@ -97,11 +97,24 @@ hipError_t select_hist1(const float* scores, const SelectPlan& p, void* ws, hipS
 hipError_t select_finish(const float* scores, const SelectPlan& p, void* ws, int32_t* idx,
                          hipStream_t s);
 
-// Few long rows (at most kSelectFewRows): sample threshold, candidate collection
-// and an exact select over the candidates (select_few.hip).
+// Few long rows (at most kSelectFewRows), select_few.hip: a histogram of the top
+// 12 bits of each row's order keys (kFewHistBins u32 counters per row, rows
+// FewHist::row_words apart) names the bin of the k-th key; the keys of that bin
+// and above are collected and selected exactly.  Sequence: select_few_prepare
+// (zero the counters), the histogram (fused into the decode scan, or
+// select_few_hist_scores over given scores), select_few_finish.
 constexpr int64_t kSelectFewRows = 256;
+constexpr int kFewHistBins = 4096;
+constexpr int kFewHistOffset = 4;            // u32 words before a row's histogram
+struct FewHist {
+  uint32_t* base;                            // histogram of row 0
+  int64_t row_words;                         // u32 words between rows
+};
 size_t select_few_ws_bytes(int64_t rows);
-hipError_t select_few(const float* scores, const SelectPlan& p, void* ws, int32_t* idx, hipStream_t s);
+FewHist select_few_hist(void* ws);
+hipError_t select_few_prepare(void* ws, int64_t rows, hipStream_t s);
+hipError_t select_few_hist_scores(const float* scores, const SelectPlan& p, void* ws, hipStream_t s);
+hipError_t select_few_finish(const float* scores, const SelectPlan& p, void* ws, int32_t* idx, hipStream_t s);
 
 hipError_t indexer_scores_f32(const dsa_indexer_args& a, int64_t row0, int64_t rows, float* out,
                               int64_t out_row_stride, hipStream_t s);
@@ -113,8 +126,9 @@ hipError_t indexer_scores_mfma(const dsa_indexer_args& a, int64_t row0, int64_t 
 constexpr int kTopkWaveSlots = 2048;
 size_t topk_fused_ws_bytes();
 hipError_t indexer_topk_fused(const dsa_indexer_args& a, int32_t k, int32_t* idx, void* ws, hipStream_t s);
-// Decode-shaped scan: fp32 scores of every (row, s) into `scores` [batch*n_q, n_k].
-hipError_t indexer_scan(const dsa_indexer_args& a, float* scores, hipStream_t s);
+// Decode-shaped scan: fp32 scores of every (row, s) into `scores` [batch*n_q, n_k],
+// plus each row's key histogram into `hist` (zeroed beforehand) when given.
+hipError_t indexer_scan(const dsa_indexer_args& a, float* scores, const FewHist* hist, hipStream_t s);
 bool indexer_mfma_supported(const dsa_indexer_args& a);
 
 size_t sparse_attn_ws_bytes(const dsa_sparse_attn_args& a);

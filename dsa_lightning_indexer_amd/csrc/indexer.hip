@@ -52,7 +52,8 @@ struct IxParams {
   float* out;            // scores [batch, rows, n_k]
   int32_t* idx;          // [batch, n_q, topk]
   int32_t topk;
-  int64_t scan_slice;    // decode scan: keys per workgroup (a multiple of 256)
+  uint32_t* hist;        // decode scan: per-row key histograms (or null)
+  int64_t hist_rw;       // u32 words between the histograms of consecutive rows
 };
 
 // ---------------------------------------------------------------- fp32 path
@@ -140,32 +141,70 @@ struct RowState {
 };
 
 // q fragments and per-(row, head) epilogue weights of query row `gi` (flattened
-// batch*n_q index).  Heads >= H are zero rows with zero weight.
-template <int DT, int D, int HT>
+// batch*n_q index).  Heads >= H are zero rows with zero weight.  FLAT issues
+// every load unconditionally (heads past H read head 0 and are zeroed
+// afterwards), so they are all in flight together and waited for once: the
+// decode scan, whose workgroups score only a few thousand keys per row, cannot
+// afford one memory latency per weight.  The fused kernel, at its register limit,
+// keeps the conditional loads (one row per few hundred thousand MFMAs).
+template <int DT, int D, int HT, bool FLAT = false>
 __device__ __forceinline__ void load_row(const IxParams& p, int64_t gi, int lane,
                                          RowState<DT, D, HT>& rs) {
   typedef Cfg<DT, D> C;
+  typedef typename AFrag<DT>::T F;
   const uint8_t* qb = (const uint8_t*)p.q;
+  if constexpr (FLAT) {
+    float wv[HT][16], sv[HT][16];
 #pragma unroll
-  for (int h = 0; h < HT; ++h) {
-    const int head = 32 * h + (lane & 31);
-    if (head < p.heads) {
-      const uint8_t* rowp = qb + ((gi * p.heads + head) * (int64_t)D) * C::ES;
+    for (int h = 0; h < HT; ++h) {
+      const int head = 32 * h + (lane & 31);
+      const uint8_t* rowp = qb + ((gi * p.heads + (head < p.heads ? head : 0)) * (int64_t)D) * C::ES;
 #pragma unroll
       for (int ks = 0; ks < C::NKS; ++ks) rs.a[h][ks] = load_frag<DT>(rowp, ks, lane);
-    } else {
 #pragma unroll
-      for (int ks = 0; ks < C::NKS; ++ks) rs.a[h][ks] = typename AFrag<DT>::T{};
+      for (int i = 0; i < 16; ++i) {
+        const int hh = 32 * h + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        const int64_t o = gi * p.heads + (hh < p.heads ? hh : 0);
+        wv[h][i] = p.w[o];
+        if constexpr (DT == DT_FP8) sv[h][i] = p.q_scale[o];
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int hh = 32 * h + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      float cv = 0.f;
-      if (hh < p.heads) {
-        cv = p.w[gi * p.heads + hh];
-        if constexpr (DT == DT_FP8) cv *= p.q_scale[gi * p.heads + hh];
+    for (int h = 0; h < HT; ++h) {
+      if (32 * h + (lane & 31) >= p.heads) {
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) rs.a[h][ks] = F{};
       }
-      rs.c[h][i] = cv;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int hh = 32 * h + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        float cv = wv[h][i];
+        if constexpr (DT == DT_FP8) cv *= sv[h][i];
+        rs.c[h][i] = hh < p.heads ? cv : 0.f;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < HT; ++h) {
+      const int head = 32 * h + (lane & 31);
+      if (head < p.heads) {
+        const uint8_t* rowp = qb + ((gi * p.heads + head) * (int64_t)D) * C::ES;
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) rs.a[h][ks] = load_frag<DT>(rowp, ks, lane);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) rs.a[h][ks] = F{};
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int hh = 32 * h + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        float cv = 0.f;
+        if (hh < p.heads) {
+          cv = p.w[gi * p.heads + hh];
+          if constexpr (DT == DT_FP8) cv *= p.q_scale[gi * p.heads + hh];
+        }
+        rs.c[h][i] = cv;
+      }
     }
   }
 }
@@ -743,33 +782,44 @@ __global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk_kernel
 }
 
 // ---------------------------------------------------------------- decode scan
-// The grid holds about two workgroups per CU (one round, no tail); workgroup
-// (slice, row) scores keys [slice * scan_slice, (slice + 1) * scan_slice) of its
-// row, its wave w taking the 64-key stages w, w + 4, w + 8, ...
+// The grid holds about two workgroups per CU (one round, no tail).  The G
+// workgroups of a row sweep its keys together in 256-key blocks: workgroup x
+// takes blocks x, x + G, x + 2G, ... (its wave w the 64 keys w of each block), so
+// at any time the row's reads fall in one contiguous window of the cache.
 
 template <int DT, int D, int HT>
 __global__ __launch_bounds__(256, 2) void ix_scan_kernel(IxParams p) {
   typedef Cfg<DT, D> C;
+  // histogram of the top 12 bits of the scores' order keys (for the few-row select)
+  __shared__ uint32_t khist[dsa_host::kFewHistBins];
   const int wid = wave_id(), lane = threadIdx.x & 63;
   const int64_t gi = blockIdx.y;                  // flattened (batch, query row)
   const int b = (int)(gi / p.n_q);
   const int64_t i = gi % p.n_q;
   const int64_t t = p.q_pos0 + i;
   const int64_t len = t + 1 < p.n_k ? t + 1 : p.n_k;
-  const int64_t slice0 = (int64_t)blockIdx.x * p.scan_slice;
-  if (slice0 >= len) return;
-  const int64_t slice1 = slice0 + p.scan_slice < len ? slice0 + p.scan_slice : len;
-  const int nstages = (int)((slice1 - slice0 + 4 * kTileKeys - 1) / (4 * kTileKeys));
-  RowState<DT, D, HT> rs;
-  load_row<DT, D, HT>(p, gi, lane, rs);
+  const int64_t nblk = (len + 4 * kTileKeys - 1) / (4 * kTileKeys);
+  if ((int64_t)blockIdx.x >= nblk) return;
+  const int nstages = (int)((nblk - blockIdx.x + gridDim.x - 1) / gridDim.x);
+  const bool hist = p.hist != nullptr;
+  if (hist) {
+    for (int i = threadIdx.x; i < dsa_host::kFewHistBins; i += 256) khist[i] = 0u;
+    __syncthreads();
+  }
   const uint8_t* kbase = (const uint8_t*)p.k + (int64_t)b * p.k_bs * C::ES;
   const float* ksc = (DT == DT_FP8) ? p.k_scale + (int64_t)b * p.ks_bs : nullptr;
   float* out = p.out + gi * (int64_t)p.n_k;
-  // B operands straight from HBM, one stage (64 keys) ahead of the MFMAs;
-  // rows past the end read key len-1 (masked on output).
+  // B operands and (fp8) key scales straight from HBM, one stage (64 keys) ahead
+  // of the MFMAs.  The next stage is loaded unconditionally (rows past the end
+  // read key len-1 and are masked on output): under a condition, the wait before
+  // the MFMAs would have to assume the younger loads absent and drain them along
+  // with the current stage.
   typedef typename AFrag<DT>::T F;
-  auto load_stage = [&](int st, F (&bf)[2][C::NKS]) {
-    const int64_t s0 = slice0 + (int64_t)(wid + 4 * st) * kTileKeys;
+  auto stage_key0 = [&](int st) {
+    return ((int64_t)st * gridDim.x + blockIdx.x) * (4 * kTileKeys) + (int64_t)wid * kTileKeys;
+  };
+  auto load_stage = [&](int st, F (&bf)[2][C::NKS], float& kscale) {
+    const int64_t s0 = stage_key0(st);
     const int64_t srow = s0 + (lane & 31);
     const int64_t s_a = srow < len ? srow : len - 1;
     const int64_t s_b = srow + 32 < len ? srow + 32 : len - 1;
@@ -778,53 +828,83 @@ __global__ __launch_bounds__(256, 2) void ix_scan_kernel(IxParams p) {
       bf[0][ks] = load_frag<DT>(kbase + s_a * C::ROWB, ks, lane);
       bf[1][ks] = load_frag<DT>(kbase + s_b * C::ROWB, ks, lane);
     }
-  };
-  // prefetch only where the second set of operands fits the register budget
-  // (64 heads of bf16 d=128 would spill)
-  constexpr bool kPrefetch = 2 * C::NKS * sizeof(F) <= 128;
-  F cur[2][C::NKS], nxt[2][C::NKS];
-  if constexpr (kPrefetch) load_stage(0, cur);
-#pragma unroll 1
-  for (int st = 0; st < nstages; ++st) {
-    const int64_t s0 = slice0 + (int64_t)(wid + 4 * st) * kTileKeys;
-    if (s0 >= slice1) break;
-    if constexpr (kPrefetch) {
-      if (st + 1 < nstages && s0 + 4 * kTileKeys < slice1) load_stage(st + 1, nxt);
-    } else {
-      load_stage(st, cur);
+    if constexpr (DT == DT_FP8) {
+      const int64_t sk = s0 + lane;
+      kscale = ksc[sk < len ? sk : len - 1];
     }
-    f32x16 acc[HT][2];
+  };
+  RowState<DT, D, HT> rs;
+  // scores of stage st from its operands bf (key scales kscale)
+  // (the two 32-key halves one after the other: half the accumulators live, and
+  // the first half's head-sum epilogue overlaps the second half's MFMAs)
+  auto score_stage = [&](int st, const F (&bf)[2][C::NKS], float kscale) {
+    float pp[2];
 #pragma unroll
-    for (int h = 0; h < HT; ++h) { acc[h][0] = f32x16{}; acc[h][1] = f32x16{}; }
+    for (int n = 0; n < 2; ++n) {
+      f32x16 acc[HT];
 #pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) {
+      for (int h = 0; h < HT; ++h) acc[h] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < C::NKS; ++ks) {
+#pragma unroll
+        for (int h = 0; h < HT; ++h) acc[h] = mfma<DT>(rs.a[h][ks], bf[n][ks], acc[h]);
+      }
+      float q = 0.f;
 #pragma unroll
       for (int h = 0; h < HT; ++h) {
-        acc[h][0] = mfma<DT>(rs.a[h][ks], cur[0][ks], acc[h][0]);
-        acc[h][1] = mfma<DT>(rs.a[h][ks], cur[1][ks], acc[h][1]);
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) q = fmaf(rs.c[h][ii], fmaxf(acc[h][ii], 0.f), q);
       }
+      pp[n] = q;
     }
-    float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-    for (int h = 0; h < HT; ++h) {
-#pragma unroll
-      for (int ii = 0; ii < 16; ++ii) {
-        p0 = fmaf(rs.c[h][ii], fmaxf(acc[h][0][ii], 0.f), p0);
-        p1 = fmaf(rs.c[h][ii], fmaxf(acc[h][1][ii], 0.f), p1);
-      }
+    float sc = combine_halves(pp[0], pp[1]);
+    const int64_t s = stage_key0(st) + lane;
+    if (s < len) {
+      if constexpr (DT == DT_FP8) sc *= kscale;
+      const float o = sc + 0.0f;
+      out[s] = o;
+      if (hist) atomicAdd(&khist[order_key(o) >> 20], 1u);
     }
-    float sc = combine_halves(p0, p1);
-    const int64_t s = s0 + lane;
-    if (s < slice1) {
-      if constexpr (DT == DT_FP8) sc *= ksc[s];
-      out[s] = sc + 0.0f;
+  };
+  // Three operand buffers used in turn, two stages in flight while one is scored
+  // (the loop body is unrolled by three, so all three are live at once and the
+  // loads go out ahead of the MFMAs); only where they fit the register budget
+  // (64 heads of bf16 d = 128 would spill: that case loads and scores one stage
+  // at a time).
+  constexpr bool kPrefetch = 2 * C::NKS * sizeof(F) <= 128;
+  F ba[2][C::NKS], bb[2][C::NKS], bc[2][C::NKS];
+  float sa = 1.f, sb = 1.f, sc3 = 1.f;
+  auto valid = [&](int st) { return st < nstages && stage_key0(st) < len; };
+  if constexpr (kPrefetch) {
+    load_stage(0, ba, sa);
+    load_stage(1, bb, sb);
+  }
+  load_row<DT, D, HT, true>(p, gi, lane, rs);
+  settle_row(rs);
+  if constexpr (kPrefetch) {
+#pragma unroll 1
+    for (int st = 0; valid(st); st += 3) {
+      load_stage(st + 2, bc, sc3);
+      score_stage(st, ba, sa);
+      if (!valid(st + 1)) break;
+      load_stage(st + 3, ba, sa);
+      score_stage(st + 1, bb, sb);
+      if (!valid(st + 2)) break;
+      load_stage(st + 4, bb, sb);
+      score_stage(st + 2, bc, sc3);
     }
-    if constexpr (kPrefetch) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks) cur[i][ks] = nxt[i][ks];
+  } else {
+#pragma unroll 1
+    for (int st = 0; valid(st); ++st) {
+      load_stage(st, ba, sa);
+      score_stage(st, ba, sa);
     }
+  }
+  if (hist) {
+    __syncthreads();
+    uint32_t* gh = p.hist + gi * p.hist_rw;
+    for (int i = threadIdx.x; i < dsa_host::kFewHistBins; i += 256)
+      if (khist[i]) atomicAdd(&gh[i], khist[i]);
   }
 }
 
@@ -901,11 +981,12 @@ hipError_t launch_scan_dt(const IxParams& p0, hipStream_t s) {
   IxParams p = p0;
   const int64_t len = p.q_pos0 + p.n_q < p.n_k ? p.q_pos0 + p.n_q : p.n_k;
   const int64_t rows = (int64_t)p.batch * p.n_q;
-  // about two workgroups per CU over all rows, slices of whole 256-key groups
+  // about two workgroups per CU over all rows (at most one per 256-key block)
   int64_t per_row = (persistent_blocks() + rows - 1) / rows;
+  const int64_t nblk = (len + 4 * kTileKeys - 1) / (4 * kTileKeys);
+  if (per_row > nblk) per_row = nblk;
   if (per_row < 1) per_row = 1;
-  p.scan_slice = ((len + per_row - 1) / per_row + 255) / 256 * 256;
-  dim3 grid((unsigned)((len + p.scan_slice - 1) / p.scan_slice), (unsigned)rows);
+  dim3 grid((unsigned)per_row, (unsigned)rows);
   if (p.heads > 32) {
     hipLaunchKernelGGL((ix_scan_kernel<DT, D, 2>), grid, dim3(256), 0, s, p);
   } else {
@@ -973,9 +1054,13 @@ hipError_t indexer_topk_fused(const dsa_indexer_args& a, int32_t k, int32_t* idx
   return hipErrorInvalidValue;
 }
 
-hipError_t indexer_scan(const dsa_indexer_args& a, float* scores, hipStream_t s) {
+hipError_t indexer_scan(const dsa_indexer_args& a, float* scores, const FewHist* hist, hipStream_t s) {
   IxParams p = make_params(a);
   p.out = scores;
+  if (hist) {
+    p.hist = hist->base;
+    p.hist_rw = hist->row_words;
+  }
   if (a.dtype == DSA_BF16) {
     if (a.dim == 128) return launch_scan_dt<DT_BF16, 128>(p, s);
     if (a.dim == 64) return launch_scan_dt<DT_BF16, 64>(p, s);

@@ -153,3 +153,52 @@ def test_searched_47_layer_pattern_on_gpu(dsa, dev, retention):
             assert np.array_equal(specs[l]["idx_out"][0].cpu().numpy(), Ts[l]), f"layer {l + 1} index"
         got = specs[l]["sa"]["out"][0].cpu().numpy()[rows]
         assert H.attn_close(got, outs[l]) <= H.ATTN_RTOL, f"layer {l + 1} attention"
+
+
+def test_decode_stack_graph_replay(dsa, dev):
+    """The decode layer loop captured once in a HIP graph and replayed: every
+    replay (with eager writes over the outputs and host synchronisation between
+    replays) reproduces the eager run bit for bit, and the eager run matches the
+    oracle on the F layers' index tensors."""
+    pattern, B, S, topk = "FSSSFSSSF", 2, 6000, 2048
+    specs, ixs = [], []
+    for l, c in enumerate(pattern):
+        sa = syn.c5_layer_sa(l, B=B, S=S, device=dev)
+        out = torch.zeros((B, 1, 16, 512), device=dev)
+        spec = {"sa": {"q": sa.q, "kv": sa.kv, "scale": sa.scale, "out": out, "d_v": 512}}
+        ix = syn.c5_layer_indexer(l, B=B, S=S, device=dev, values="int") if c == "F" else None
+        ixs.append(ix)
+        if ix is not None:
+            spec["ix"] = {"q": ix.q, "k": ix.k, "w": ix.w, "q_scale": ix.q_scale, "k_scale": ix.k_scale,
+                          "q_pos0": ix.q_pos0}
+            spec["idx_out"] = torch.empty((B, 1, topk), dtype=torch.int32, device=dev)
+        specs.append(spec)
+    ws = torch.empty(max(dsa.indexcache_forward_workspace_size(pattern, specs, topk), 256),
+                     dtype=torch.uint8, device=dev)
+    dsa.indexcache_forward(pattern, specs, topk, ws=ws)
+    torch.cuda.synchronize()
+    eager_idx = [s["idx_out"].clone() for s in specs if "idx_out" in s]
+    eager_out = [s["sa"]["out"].clone() for s in specs]
+    for l, c in enumerate(pattern):
+        if c == "F":
+            q, k, w = H.indexer_f64(ixs[l], 1)
+            T = oracle.indexer_topk(q, k, w, topk, q_pos0=S - 1)[0]
+            assert np.array_equal(specs[l]["idx_out"][1].cpu().numpy(), T)
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dsa.indexcache_forward(pattern, specs, topk, ws=ws)
+    for rep in range(3):
+        for s in specs:
+            s["sa"]["out"].fill_(float("nan"))
+            if "idx_out" in s:
+                s["idx_out"].fill_(-7)
+        ws.fill_(0xA5)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got_idx = [s["idx_out"] for s in specs if "idx_out" in s]
+        for a, b in zip(got_idx, eager_idx):
+            assert torch.equal(a, b), f"replay {rep}: index tensor differs from the eager run"
+        for l, s in enumerate(specs):
+            assert torch.equal(s["sa"]["out"], eager_out[l]), f"replay {rep}: layer {l + 1} attention differs"

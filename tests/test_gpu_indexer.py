@@ -162,28 +162,34 @@ def test_select_from_given_scores_with_ties(dsa, dev):
             assert np.array_equal(got[b, i], ref), (b, i)
 
 
-def test_select_few_rows_threshold_and_fallbacks(dsa, dev):
-    """Few long rows go through the sampled-threshold select.  Row 0: ordinary
-    float scores (candidate path).  Row 1: the first 200 of the sampler's 512
-    runs of 16 positions (spread evenly: run j starts at j * (n - 16) // 511)
-    hold very high scores, so fewer than k keys reach the sample's threshold
-    and the whole-row select runs.  Row 2: all scores equal, so every key
-    reaches the threshold (more than the candidate buffer holds): whole-row
-    select again, ties broken by position.  Exact against the oracle."""
+def test_select_few_rows_histogram_paths(dsa, dev):
+    """Few long rows go through the key-histogram select (the bin of the k-th
+    key, its candidates, an exact select over them).  Rows: 0 ordinary float
+    scores; 1 a crowded k-th bin (6000 scores in [3, 3.01): one 12-bit key bin
+    that still fits the candidate buffer); 2 all scores equal (more candidates
+    than the buffer holds: whole-row select, ties by position); 3 integer scores
+    0..49 (thousands of ties at the k-th key spread over every chunk); 4
+    increasing scores (every candidate in the last chunk); 5 negative scores only.
+    Exact against the oracle."""
     g = torch.Generator(device=dev).manual_seed(13)
-    n_k, topk = 204800, 2048
-    sc = torch.randn((3, 1, n_k), generator=g, device=dev)
-    gap = (n_k - 16) // 511
-    pos = (torch.arange(200, device=dev).view(-1, 1) * gap + torch.arange(16, device=dev).view(1, -1)).flatten()
-    sc[1, 0, pos] = 100.0 + torch.arange(pos.numel(), device=dev).float()
+    n_k, topk, R = 204800, 2048, 6
+    sc = torch.randn((R, 1, n_k), generator=g, device=dev)
+    crowd = torch.randperm(n_k, generator=g, device=dev)[:6000]
+    sc[1, 0, crowd] = 3.0 + 0.01 * torch.rand(6000, generator=g, device=dev)
     sc[2, 0] = 0.5
-    dummy_q = torch.zeros((3, 1, 1, 32), dtype=torch.bfloat16, device=dev)
-    dummy_k = torch.zeros((3, n_k, 32), dtype=torch.bfloat16, device=dev)
-    dummy_w = torch.zeros((3, 1, 1), device=dev)
+    sc[3, 0] = torch.randint(0, 50, (n_k,), generator=g, device=dev).float()
+    sc[4, 0] = torch.arange(n_k, device=dev).float() / n_k
+    sc[5, 0] = -1.0 - torch.rand(n_k, generator=g, device=dev)
+    dummy_q = torch.zeros((R, 1, 1, 32), dtype=torch.bfloat16, device=dev)
+    dummy_k = torch.zeros((R, n_k, 32), dtype=torch.bfloat16, device=dev)
+    dummy_w = torch.zeros((R, 1, 1), device=dev)
     got = dsa.topk(dummy_q, dummy_k, dummy_w, topk, q_pos0=n_k - 1, scores=sc).cpu().numpy()
     s64 = sc.cpu().double().numpy()
-    for b in range(3):
+    for b in range(R):
         assert np.array_equal(got[b, 0], oracle.topk_row(s64[b, 0], topk)), b
+    # a second call gives the same rows
+    again = dsa.topk(dummy_q, dummy_k, dummy_w, topk, q_pos0=n_k - 1, scores=sc).cpu().numpy()
+    assert np.array_equal(again, got)
 
 
 # --------------------------------------------------------------------------- decode scan
