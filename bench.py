@@ -48,9 +48,10 @@ def parse():
     p.add_argument("--sweep", action="store_true",
                    help="retention sweep instead of the bench line: both stacks under all-F, uniform 1/2, 1/4, "
                         "1/8 and (decode) the searched 47-layer patterns; prints one JSON object")
-    p.add_argument("--profile", choices=["indexer", "copy"], default=None,
+    p.add_argument("--profile", choices=["indexer", "attn", "copy"], default=None,
                    help="counter-collection runs: 'indexer' launches only the prefill F layer's fused "
-                        "indexer+Top-k (3 launches, the first a warm-up); 'copy' runs a 1 GiB read + "
+                        "indexer+Top-k (3 launches, the first a warm-up); 'attn' that layer's prefill "
+                        "sparse attention (3 launches after one indexer launch); 'copy' runs a 1 GiB read + "
                         "1 GiB write elementwise kernel, the calibration for the HBM byte counters")
     return p.parse_args()
 
@@ -173,6 +174,17 @@ def profile_run(args, dev):
     import dsa_lightning_indexer_amd as dsa
     from synth import inputs as syn
     L = args.prefill_len
+    if args.profile == "attn":
+        # the step's first prefill layer: its sparse attention over its F layer's index tensor
+        ix, sa = syn.c4_stack(L=L, n_layers=1, seed=4, device=dev)[0]
+        idx = dsa.topk(ix.q, ix.k, ix.w, 2048)
+        out = torch.empty((1, L, 16, 512), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        for i in range(3):
+            dsa.sparse_attn(sa.q, sa.kv, idx, sa.scale, d_v=512, out=out)
+            torch.cuda.synchronize()
+            print(f"profile attn: prefill sparse attention L={L} launch {i + 1}/3 done", flush=True)
+        return
     ix = syn.c4_stack(L=L, n_layers=1, seed=4, device=dev, with_sa=False)[0][0]   # the step's first F layer
     out = torch.empty((1, L, 2048), dtype=torch.int32, device=dev)
     torch.cuda.synchronize()

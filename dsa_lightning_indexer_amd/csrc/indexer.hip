@@ -448,19 +448,68 @@ constexpr int kCandCap = 16384;        // candidates per row before a compaction
 __device__ __forceinline__ u32x4 ld4(const uint32_t* p, int j) { return *(const u32x4*)(p + j); }
 
 // The select passes stream the candidate buffer from L2 with kSelVec 16-byte
-// loads in flight per lane (1024-2048 entries per wave step).
+// loads in flight per lane (1024-2048 entries per wave step).  They are kept out
+// of line: a call returns with its memory operations complete, whereas inlined,
+// the compaction's stores would still be counted as outstanding at the top of
+// the tile loop, where the compiler would then wait for every vector memory
+// operation -- the tile loads in flight included -- on every tile.
 constexpr int kSelVec = 8;
 
-// One radix pass: histogram of the 8-bit digit at `shift` among entries whose
-// masked key equals `prefix`; then pick the digit holding the rem-th largest.
-// Returns the digit; rem becomes the rank inside that digit's bucket and
-// *bucket the bucket's size.
-__device__ uint32_t wave_radix_pass(const uint32_t* cu, int n, uint32_t prefix, uint32_t mask, int shift,
-                                    uint32_t& rem, uint32_t* bucket, uint32_t* hist, int lane) {
+// Result of a radix pass: the digit holding the rem-th largest key, the rank
+// of that key inside the digit's bucket and the bucket's size.  (The select
+// helpers take and return values only: a reference or pointer to a local
+// would put it in scratch memory, and the tile loop would then reload the
+// threshold from there, behind waits for every vector memory operation.)
+struct RadixPick {
+  uint32_t digit, rem, bucket;
+};
+// One radix pass: histogram of the 8-bit digit at SHIFT among entries whose
+// masked key equals `prefix`; then pick the digit holding the rem-th largest.  Full steps load without bounds checks.  The top
+// byte (sign and high exponent bits) is nearly the same for every key of a row:
+// that pass counts the entries whose top byte equals the first entry's in a
+// register, four entries per compare, and sends only the others to LDS atomics
+// (same-address LDS atomics serialise, and this code shares its SIMD with the
+// MFMA stream of the other workgroup, where every instruction counts).
+template <int SHIFT>
+__device__ __attribute__((noinline)) RadixPick wave_radix_pass(const uint32_t* cu, int n, uint32_t prefix,
+                                                               uint32_t mask, uint32_t rem, uint32_t* hist, int lane) {
+  constexpr int STEP = 64 * 4 * kSelVec;
 #pragma unroll
   for (int j = 0; j < 4; ++j) hist[lane * 4 + j] = 0u;
   lds_sync();
-  for (int j0 = 0; j0 < n; j0 += 64 * 4 * kSelVec) {
+  const uint32_t d0 = SHIFT == 24 ? (uint32_t)__builtin_amdgcn_readfirstlane((int)cu[0]) >> 24 : 0u;
+  const uint32_t base = d0 << 24;
+  uint32_t same = 0;
+  auto count = [&](const u32x4& v, int jb) {
+    if constexpr (SHIFT == 24) {
+      const uint32_t x = (v[0] ^ base) | (v[1] ^ base) | (v[2] ^ base) | (v[3] ^ base);
+      if ((x >> 24) == 0u && jb + 4 <= n) {
+        same += 4u;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (jb + e < n) {
+            const uint32_t d = v[e] >> 24;
+            if (d == d0) ++same;
+            else atomicAdd(&hist[d], 1u);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (jb + e < n && (v[e] & mask) == prefix) atomicAdd(&hist[(v[e] >> SHIFT) & 255u], 1u);
+    }
+  };
+  int j0 = 0;
+  for (; j0 + STEP <= n; j0 += STEP) {
+    u32x4 u[kSelVec];
+#pragma unroll
+    for (int r = 0; r < kSelVec; ++r) u[r] = ld4(cu, j0 + 4 * (r * 64 + lane));
+#pragma unroll
+    for (int r = 0; r < kSelVec; ++r) count(u[r], j0 + 4 * (r * 64 + lane));
+  }
+  if (j0 < n) {
     u32x4 u[kSelVec];
 #pragma unroll
     for (int r = 0; r < kSelVec; ++r) {
@@ -468,30 +517,12 @@ __device__ uint32_t wave_radix_pass(const uint32_t* cu, int n, uint32_t prefix, 
       u[r] = j < n ? ld4(cu, j) : u32x4{};
     }
 #pragma unroll
-    for (int r = 0; r < kSelVec; ++r) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = j0 + 4 * (r * 64 + lane) + e;
-        const bool in = j < n && (u[r][e] & mask) == prefix;
-        const uint32_t d = (u[r][e] >> shift) & 255u;
-        if (shift != 24) {
-          if (in) atomicAdd(&hist[d], 1u);
-          continue;
-        }
-        // Top byte (sign and high exponent bits): nearly all keys share one
-        // digit, so the first active lane's digit is counted with a single
-        // add and only the other lanes use atomics (same-address LDS atomics
-        // serialise).
-        const uint64_t act = ballot(in);
-        if (act) {
-          const int lead = (int)__builtin_ctzll(act);
-          const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)d, lead);
-          const uint64_t same = ballot(in && d == d0);
-          if (lane == lead) atomicAdd(&hist[d0], (uint32_t)__builtin_popcountll(same));
-          else if (in && d != d0) atomicAdd(&hist[d], 1u);
-        }
-      }
-    }
+    for (int r = 0; r < kSelVec; ++r) count(u[r], j0 + 4 * (r * 64 + lane));
+  }
+  if constexpr (SHIFT == 24) {
+    uint32_t tot;
+    wave_excl_scan(same, &tot);
+    if (lane == 0 && tot) atomicAdd(&hist[d0], tot);
   }
   lds_sync();
   // lane owns bins 255-4*lane .. 252-4*lane (descending)
@@ -511,21 +542,65 @@ __device__ uint32_t wave_radix_pass(const uint32_t* cu, int n, uint32_t prefix, 
     }
   }
   const int src = __builtin_ctzll(ballot(mine));
-  digit = __shfl(digit, src, 64);
-  rem = __shfl(nrem, src, 64);
-  *bucket = __shfl(bsz, src, 64);
+  RadixPick r;
+  r.digit = (uint32_t)__builtin_amdgcn_readlane((int)digit, src);
+  r.rem = (uint32_t)__builtin_amdgcn_readlane((int)nrem, src);
+  r.bucket = (uint32_t)__builtin_amdgcn_readlane((int)bsz, src);
   lds_sync();
-  return digit;
+  return r;
 }
 
-// Stable in-place compaction of cu/ci[0..n): keeps entries with key > T, plus
-// (when tie_limit >= 0) the first tie_limit entries with key == T, or (when
-// tie_limit < 0) every entry with key == T.  With out_idx set, the kept
-// positions go there instead (at most `limit`).  Returns the number kept.
-// Each lane takes 4 consecutive entries per block; ranks in buffer order come
-// from one ballot per entry slot.  A step loads all its blocks before it
-// writes, and an entry is never written past its own slot, so in place is safe.
-__device__ int wave_keep(uint32_t* cu, uint32_t* ci, int n, uint32_t T, int64_t tie_limit, int lane,
+// Stable in-place compaction of cu/ci[0..n) keeping every entry with key >= T
+// (a shrink).  Each lane takes 4 consecutive entries per block; ranks in buffer
+// order come from one ballot per entry slot.  A step loads all its blocks
+// before it writes, and an entry is never written past its own slot, so in
+// place is safe.  Returns the number kept.
+__device__ __attribute__((noinline)) int wave_keep_ge(uint32_t* cu, uint32_t* ci, int n, uint32_t T, int lane) {
+  constexpr int R = kSelVec;
+  int out = 0;
+  for (int j0 = 0; j0 < n; j0 += 64 * 4 * R) {
+    const bool full = j0 + 64 * 4 * R <= n;
+    u32x4 u[R], id[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int j = j0 + 4 * (r * 64 + lane);
+      const bool ok = full || j < n;
+      u[r] = ok ? ld4(cu, j) : u32x4{};
+      id[r] = ok ? ld4(ci, j) : u32x4{};
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int jb = j0 + 4 * (r * 64 + lane);
+      bool keep[4];
+      uint64_t km[4];
+      uint32_t kb = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        keep[e] = (full || jb + e < n) && u[r][e] >= T;
+        km[e] = ballot(keep[e]);
+        kb += lanes_below(km[e]);
+      }
+      int d = out + (int)kb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (keep[e]) {
+          cu[d] = u[r][e];
+          ci[d] = id[r][e];
+          ++d;
+        }
+        out += __builtin_popcountll(km[e]);
+      }
+    }
+  }
+  lds_sync();
+  return out;
+}
+
+// Stable in-place compaction of cu/ci[0..n): keeps entries with key > T plus the
+// first tie_limit entries with key == T.  With out_idx set, the kept positions
+// go there instead (at most `limit`).  Returns the number kept.  Same blocking
+// as wave_keep_ge.
+__device__ __attribute__((noinline)) int wave_keep(uint32_t* cu, uint32_t* ci, int n, uint32_t T, int64_t tie_limit, int lane,
                          int32_t* out_idx, int limit) {
   constexpr int R = kSelVec;
   int out = 0;
@@ -554,7 +629,7 @@ __device__ int wave_keep(uint32_t* cu, uint32_t* ci, int n, uint32_t T, int64_t 
       uint32_t kb = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        keep[e] = jb + e < n && (u[r][e] > T || (tie[e] && (tie_limit < 0 || trank < tie_limit)));
+        keep[e] = jb + e < n && (u[r][e] > T || (tie[e] && trank < tie_limit));
         trank += tie[e] ? 1 : 0;
         km[e] = ballot(keep[e]);
         kb += lanes_below(km[e]);
@@ -582,45 +657,42 @@ __device__ int wave_keep(uint32_t* cu, uint32_t* ci, int n, uint32_t T, int64_t 
   return out;
 }
 
-// Exact k-th largest key T among cu[0..n) and how many entries equal to T fit.
-__device__ void wave_select_exact(const uint32_t* cu, int n, int k, uint32_t* hist, int lane, uint32_t& T,
-                                  uint32_t& req) {
-  uint32_t prefix = 0, mask = 0, rem = (uint32_t)k, bucket;
-#pragma unroll 1
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    const uint32_t d = wave_radix_pass(cu, n, prefix, mask, shift, rem, &bucket, hist, lane);
-    prefix |= d << shift;
-    mask |= 0xFFu << shift;
-  }
-  T = prefix;
-  req = rem;
+// Exact k-th largest key T among cu[0..n) and how many entries equal to T fit
+// (T and that count in `rem`).
+struct ExactPick {
+  uint32_t T, req;
+};
+__device__ __attribute__((noinline)) ExactPick wave_select_exact(const uint32_t* cu, int n, int k, uint32_t* hist,
+                                                                 int lane) {
+  const RadixPick a = wave_radix_pass<24>(cu, n, 0u, 0u, (uint32_t)k, hist, lane);
+  const uint32_t p1 = a.digit << 24;
+  const RadixPick b = wave_radix_pass<16>(cu, n, p1, 0xFF000000u, a.rem, hist, lane);
+  const uint32_t p2 = p1 | (b.digit << 16);
+  const RadixPick c = wave_radix_pass<8>(cu, n, p2, 0xFFFF0000u, b.rem, hist, lane);
+  const uint32_t p3 = p2 | (c.digit << 8);
+  const RadixPick d = wave_radix_pass<0>(cu, n, p3, 0xFFFFFF00u, c.rem, hist, lane);
+  return ExactPick{p3 | d.digit, d.rem};
 }
 
 // Shrink a full buffer while keeping every entry that can still be in the row's
 // Top-k.  First try the 16-bit prefix of the k-th key (two passes): keep every
 // entry at or above it; new arrivals must then be >= that prefix.  If ties or a
 // crowded bucket leave the buffer too full, select exactly (k entries kept,
-// arrivals must beat T strictly: a later position loses a tie).
-__device__ int wave_shrink(uint32_t* cu, uint32_t* ci, int n, int k, uint32_t* hist, int lane,
-                           uint32_t& thr, bool& strict) {
-  uint32_t rem = (uint32_t)k, bucket;
-  const uint32_t d1 = wave_radix_pass(cu, n, 0u, 0u, 24, rem, &bucket, hist, lane);
-  const uint32_t d2 = wave_radix_pass(cu, n, d1 << 24, 0xFF000000u, 16, rem, &bucket, hist, lane);
-  const uint32_t P = (d1 << 24) | (d2 << 16);
-  const int kept = (k - (int)rem) + (int)bucket;          // entries with key >= P
-  if (kept <= n - n / 4) {
-    const int m = wave_keep(cu, ci, n, P, -1, lane, nullptr, n);   // key > P or == P ...
-    // wave_keep with tie_limit < 0 keeps key >= P exactly; entries in (P, P+0xFFFF] are > P.
-    thr = P;
-    strict = false;
-    return m;
-  }
-  uint32_t T, req;
-  wave_select_exact(cu, n, k, hist, lane, T, req);
-  const int m = wave_keep(cu, ci, n, T, (int64_t)req, lane, nullptr, n);
-  thr = T;
-  strict = true;
-  return m;
+// arrivals must beat T strictly: a later position loses a tie).  Returns the
+// entries kept, the new threshold and whether arrivals must beat it strictly.
+struct Shrunk {
+  int n;
+  uint32_t thr;
+  bool strict;
+};
+__device__ __forceinline__ Shrunk wave_shrink(uint32_t* cu, uint32_t* ci, int n, int k, uint32_t* hist, int lane) {
+  const RadixPick a = wave_radix_pass<24>(cu, n, 0u, 0u, (uint32_t)k, hist, lane);
+  const RadixPick b = wave_radix_pass<16>(cu, n, a.digit << 24, 0xFF000000u, a.rem, hist, lane);
+  const uint32_t P = (a.digit << 24) | (b.digit << 16);
+  const int kept = (k - (int)b.rem) + (int)b.bucket;          // entries with key >= P
+  if (kept <= n - n / 4) return Shrunk{wave_keep_ge(cu, ci, n, P, lane), P, false};
+  const ExactPick e = wave_select_exact(cu, n, k, hist, lane);
+  return Shrunk{wave_keep(cu, ci, n, e.T, (int64_t)e.req, lane, nullptr, n), e.T, true};
 }
 
 // ---------------------------------------------------------------- prefill kernels
@@ -747,7 +819,10 @@ __global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk_kernel
           const uint32_t u = order_key(v);
           if (cnt + 64 > kCandCap) {
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-            cnt = wave_shrink(cu, ci, cnt, k, hist[wid], lane, thr, strict);
+            const Shrunk sh = wave_shrink(cu, ci, cnt, k, hist[wid], lane);
+            cnt = sh.n;
+            thr = sh.thr;
+            strict = sh.strict;
             full = true;
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
           }
@@ -767,9 +842,8 @@ __global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk_kernel
       int32_t* out = p.idx + gi * (int64_t)k;
       int nout;
       if (cnt > k) {
-        uint32_t T, req;
-        wave_select_exact(cu, cnt, k, hist[wid], lane, T, req);
-        nout = wave_keep(cu, ci, cnt, T, (int64_t)req, lane, out, k);
+        const ExactPick e = wave_select_exact(cu, cnt, k, hist[wid], lane);
+        nout = wave_keep(cu, ci, cnt, e.T, (int64_t)e.req, lane, out, k);
         nout = nout < k ? nout : k;
       } else {
         for (int j = lane; j < cnt; j += 64) out[j] = (int32_t)ci[j];
