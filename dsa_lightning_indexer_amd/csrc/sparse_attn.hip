@@ -314,39 +314,37 @@ __global__ __launch_bounds__(256, 3) void sa_mla4_kernel(SAParams p) {
   }
 }
 
-// Merge the split partials of one (query row, head): weights exp(m_s - M) are
-// computed once into LDS, then each thread accumulates its output columns.
-__global__ __launch_bounds__(256) void sa_combine_kernel(SAParams p) {
+// Merge the split partials of one (query row, head): thread c loads column c of
+// every split's partial output first (all loads in flight at once), while wave
+// 0 forms the weights exp(m_s - M) in LDS; then each thread sums its column.
+constexpr int kMaxSplit = kMaxTopk / 64;    // splits hold at least 64 positions
+__global__ __launch_bounds__(512) void sa_combine_kernel(SAParams p) {
   __shared__ float wsum[2];
-  __shared__ float wgt[128];
+  __shared__ float wgt[kMaxSplit];
   const int h = blockIdx.x % p.heads;
   const int64_t gi = blockIdx.x / p.heads;
   const float* ml = p.ws_ml + (gi * p.nsplit * p.heads + h) * 2;   // split stride: heads * 2
+  const float* po = p.ws_o + (gi * p.nsplit * p.heads + h) * (int64_t)p.d_v;
+  const int64_t sstride = (int64_t)p.heads * p.d_v;
+  const int c = threadIdx.x;                 // one output column per thread (d_v = blockDim.x)
+  float v[kMaxSplit];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplit; ++sp) v[sp] = sp < p.nsplit ? po[sp * sstride + c] : 0.f;
   if (threadIdx.x < 64) {
-    float m = -__builtin_inff();
-    for (int sp = threadIdx.x; sp < p.nsplit; sp += 64) m = fmaxf(m, ml[(int64_t)sp * p.heads * 2]);
-    const float M = wave_max(m);
-    float L = 0.f;
-    for (int sp = threadIdx.x; sp < p.nsplit; sp += 64) {
-      const float ms = ml[(int64_t)sp * p.heads * 2];
-      const float w = (ms == -__builtin_inff()) ? 0.f : __expf(ms - M);
-      wgt[sp] = w;
-      L += w * ml[(int64_t)sp * p.heads * 2 + 1];
-    }
-    L = wave_sum(L);
+    const float ms = (int)threadIdx.x < p.nsplit ? ml[(int64_t)threadIdx.x * p.heads * 2] : -__builtin_inff();
+    const float ls = (int)threadIdx.x < p.nsplit ? ml[(int64_t)threadIdx.x * p.heads * 2 + 1] : 0.f;
+    const float M = wave_max(ms);
+    const float w = (ms == -__builtin_inff()) ? 0.f : __expf(ms - M);
+    if ((int)threadIdx.x < kMaxSplit) wgt[threadIdx.x] = w;
+    const float L = wave_sum(w * ls);
     if (threadIdx.x == 0) wsum[0] = L > 0.f ? 1.f / L : 0.f;
   }
   __syncthreads();
-  const float inv = wsum[0];
-  const float* po = p.ws_o + (gi * p.nsplit * p.heads + h) * (int64_t)p.d_v;
-  const int64_t sstride = (int64_t)p.heads * p.d_v;
-  float* out = p.out + (gi * p.heads + h) * (int64_t)p.d_v;
-  for (int c = threadIdx.x; c < p.d_v; c += blockDim.x) {
-    float acc = 0.f;
-#pragma unroll 8
-    for (int sp = 0; sp < p.nsplit; ++sp) acc = fmaf(wgt[sp], po[sp * sstride + c], acc);
-    out[c] = acc * inv;
-  }
+  float acc = 0.f;
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplit; ++sp)
+    if (sp < p.nsplit) acc = fmaf(wgt[sp], v[sp], acc);
+  p.out[(gi * p.heads + h) * (int64_t)p.d_v + c] = acc * wsum[0];
 }
 
 bool mla_ok(const dsa_sparse_attn_args& a) {
@@ -401,7 +399,7 @@ hipError_t sparse_attn_launch(const dsa_sparse_attn_args& a, void* ws, hipStream
     dim3 grid((unsigned)(rows * p.nsplit));
     hipLaunchKernelGGL((sa_mla4_kernel<576, 512>), grid, dim3(256), 0, s, p);
     if (p.nsplit > 1) {
-      hipLaunchKernelGGL(sa_combine_kernel, dim3((unsigned)(rows * a.heads)), dim3(256), 0, s, p);
+      hipLaunchKernelGGL(sa_combine_kernel, dim3((unsigned)(rows * a.heads)), dim3(512), 0, s, p);
     }
     return hipGetLastError();
   }
