@@ -5,10 +5,10 @@ HIP kernels of libdsa.so.  torch provides device memory and the current HIP
 stream.  Importing fails loudly when the library has not been built.
 """
 from ._lib import (  # noqa: F401
-    LIB, LIB_PATH, DsaError, IndexerArgs, SparseAttnArgs, Layer, dtype_code, abi_version,
+    LIB, LIB_PATH, DsaError, IndexerArgs, SparseAttnArgs, Layer, DistillArgs, dtype_code, abi_version,
     indexer_args, sparse_attn_args,
 )
 from .api import (  # noqa: F401
     indexer_scores, topk, topk_workspace_size, sparse_attn, sparse_attn_workspace_size,
-    indexcache_forward, indexcache_forward_workspace_size, index_overlap,
+    indexcache_forward, indexcache_forward_workspace_size, index_overlap, indexer_distill,
 )

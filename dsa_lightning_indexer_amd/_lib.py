@@ -44,6 +44,11 @@ class Layer(ctypes.Structure):
     _fields_ = [("ix", IndexerArgs), ("sa", SparseAttnArgs), ("idx_out", c_vp)]
 
 
+class DistillArgs(ctypes.Structure):
+    _fields_ = [("ix", IndexerArgs), ("topk", c_i32), ("n_teachers", c_i32), ("idx", c_vp), ("teachers", c_vp),
+                ("loss", c_vp), ("delta", c_vp), ("dq", c_vp), ("dw", c_vp), ("dk", c_vp)]
+
+
 def _sig(name, res, *args):
     f = getattr(LIB, name)
     f.restype = res
@@ -65,10 +70,12 @@ indexcache_forward_workspace_size = _sig("indexcache_forward_workspace_size", c_
 indexcache_forward_c = _sig("indexcache_forward", c_i32, ctypes.c_char_p, c_i32, P_LAYER, c_i32,
                             ctypes.POINTER(c_i32), c_vp, c_sz, c_vp)
 dsa_index_overlap = _sig("dsa_index_overlap", c_i32, c_vp, c_vp, c_i64, c_i32, c_vp, c_vp, c_vp)
+dsa_indexer_distill = _sig("dsa_indexer_distill", c_i32, ctypes.POINTER(DistillArgs), c_vp)
 
 EXPORTS = ["dsa_abi_version", "dsa_status_string", "dsa_last_error", "dsa_indexer_scores",
            "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_attn_workspace_size", "dsa_sparse_attn",
-           "indexcache_forward_workspace_size", "indexcache_forward", "dsa_index_overlap"]
+           "indexcache_forward_workspace_size", "indexcache_forward", "dsa_index_overlap",
+           "dsa_indexer_distill"]
 
 
 class DsaError(RuntimeError):

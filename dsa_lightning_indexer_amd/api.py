@@ -119,3 +119,28 @@ def index_overlap(a, b, k, *, rows=None, row_counts=None, total=None):
                                 None if row_counts is None else row_counts.data_ptr(),
                                 total.data_ptr(), _stream()))
     return total
+
+
+def indexer_distill(q, k, w, idx, teachers, *, q_pos0=0):
+    """Distillation loss over the selected Top-k and its backward.
+    q [B, n_q, H, 128] bf16, k [B, n_k, 128] bf16, w [B, n_q, H] fp32,
+    idx [B, n_q, topk] int32, teachers [r, B, n_q, topk] fp32.
+    Returns dict(loss [B, n_q], delta [B, n_q, topk], dq [B, n_q, H, 128],
+    dw [B, n_q, H], dk [B, n_k, 128]), all fp32."""
+    B, n_q, H, d = q.shape
+    n_k = k.shape[1]
+    r, topk = teachers.shape[0], idx.shape[2]
+    dev = q.device
+    out = dict(loss=torch.empty((B, n_q), dtype=torch.float32, device=dev),
+               delta=torch.empty((B, n_q, topk), dtype=torch.float32, device=dev),
+               dq=torch.empty((B, n_q, H, d), dtype=torch.float32, device=dev),
+               dw=torch.empty((B, n_q, H), dtype=torch.float32, device=dev),
+               dk=torch.empty((B, n_k, d), dtype=torch.float32, device=dev))
+    a = L.DistillArgs()
+    a.ix = L.indexer_args(q, k, w, None, None, q_pos0)
+    a.topk, a.n_teachers = topk, r
+    a.idx, a.teachers = idx.data_ptr(), teachers.data_ptr()
+    for name in ("loss", "delta", "dq", "dw", "dk"):
+        setattr(a, name, out[name].data_ptr())
+    L.check(L.dsa_indexer_distill(ctypes.byref(a), _stream()))
+    return out

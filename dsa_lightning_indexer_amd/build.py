@@ -14,7 +14,7 @@ BUILD = os.path.join(HERE, "_build")
 ARCH = os.environ.get("DSA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["select.hip", "select_few.hip", "indexer.hip", "sparse_attn.hip", "overlap.hip", "api.cpp"]
+SOURCES = ["select.hip", "select_few.hip", "indexer.hip", "sparse_attn.hip", "overlap.hip", "distill.hip", "api.cpp"]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     # keep the compiler from emitting packed fp32 VALU ops
@@ -27,7 +27,8 @@ FLAGS = [
 # NaN-quieting v_max plus the max.
 # MFMA results stay in VGPRs (the VALU epilogue reads them directly instead of
 # copying them out of AGPRs).
-EXTRA = {"indexer.hip": ["-fno-honor-nans"], "sparse_attn.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+EXTRA = {"indexer.hip": ["-fno-honor-nans"], "sparse_attn.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "distill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src):

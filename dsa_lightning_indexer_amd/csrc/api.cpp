@@ -335,6 +335,26 @@ dsa_status indexcache_forward(const char* pattern, int32_t n, const dsa_layer* l
   return DSA_OK;
 }
 
+dsa_status dsa_indexer_distill(const dsa_distill_args* a, hipStream_t stream) {
+  g_last_error.clear();
+  if (!a) return fail(DSA_ERR_INVALID, "distillation args is NULL");
+  dsa_status st = check_indexer_shape(&a->ix);
+  if (st == DSA_OK) st = check_indexer_data(&a->ix);
+  if (st != DSA_OK) return st;
+  if (a->topk < 1 || a->topk > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID, "topk must be 1..%d", DSA_MAX_TOPK);
+  if (a->n_teachers < 1 || a->n_teachers > 8) return fail(DSA_ERR_INVALID, "n_teachers must be 1..8");
+  if (!dsa_host::distill_supported(a->ix, a->topk, a->n_teachers))
+    return fail(DSA_ERR_UNSUPPORTED, "distillation needs BF16 indexer inputs with dim 128 and at most 64 heads");
+  if (!a->idx || !a->teachers || !a->loss || !a->delta || !a->dq || !a->dw || !a->dk)
+    return fail(DSA_ERR_INVALID, "idx, teachers, loss, delta, dq, dw and dk are required");
+  if (!aligned(a->idx, 4) || !aligned(a->teachers, 4) || !aligned(a->loss, 4) || !aligned(a->delta, 4) ||
+      !aligned(a->dw, 4) || !aligned(a->dk, 4) || !aligned(a->dq, 16))
+    return fail(DSA_ERR_INVALID, "misaligned pointer (dq needs 16 bytes, the others 4)");
+  return hip_status(dsa_host::distill_launch(a->ix, a->topk, a->n_teachers, a->idx, a->teachers, a->loss,
+                                             a->delta, a->dq, a->dw, a->dk, stream),
+                    "distillation launch");
+}
+
 dsa_status dsa_index_overlap(const int32_t* a, const int32_t* b, int64_t rows, int32_t k,
                              int32_t* row_counts, unsigned long long* total, hipStream_t stream) {
   g_last_error.clear();

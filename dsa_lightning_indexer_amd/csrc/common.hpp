@@ -131,6 +131,12 @@ hipError_t indexer_topk_fused(const dsa_indexer_args& a, int32_t k, int32_t* idx
 hipError_t indexer_scan(const dsa_indexer_args& a, float* scores, const FewHist* hist, hipStream_t s);
 bool indexer_mfma_supported(const dsa_indexer_args& a);
 
+// Distillation loss over the selected Top-k and its backward (distill.hip).
+bool distill_supported(const dsa_indexer_args& a, int32_t topk, int32_t r);
+hipError_t distill_launch(const dsa_indexer_args& a, int32_t topk, int32_t r, const int32_t* idx,
+                          const float* teachers, float* loss, float* delta, float* dq, float* dw, float* dk,
+                          hipStream_t s);
+
 size_t sparse_attn_ws_bytes(const dsa_sparse_attn_args& a);
 hipError_t sparse_attn_launch(const dsa_sparse_attn_args& a, void* ws, hipStream_t s);
 

@@ -190,6 +190,52 @@ dsa_status dsa_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t
                              int32_t k, int32_t* row_counts, unsigned long long* total,
                              hipStream_t stream);
 
+/*
+ * Training-aware IndexCache: the indexer-side multi-layer distillation loss over
+ * the selected Top-k and its backward ([IC-SUMMARY] §3.2 and Proposition 1;
+ * [DSA-NOTES] §5.1-5.2, §7.1-7.3).  An F layer's indexer is distilled towards
+ * the attention distributions p^(1..r) of the r layers that use its index set.
+ * For query row (b, i) at position t with index row T (entries outside
+ * [0, min(t, n_k - 1)], e.g. the -1 padding, take no part):
+ *     z_e     = sum_j w[j] ReLU(q[j] . k[T_e])                 (indexer scores)
+ *     pi      = softmax(z)
+ *     loss    = (1/r) sum_l sum_e p_l[e] (log p_l[e] - log pi_e)   (0 log 0 = 0)
+ *     delta_e = dloss/dz_e = pi_e * sum(p_bar) - p_bar_e,  p_bar = (1/r) sum_l p_l
+ *               (= pi_e - p_bar_e when the teachers are distributions)
+ *     dw[j]   = sum_e delta_e ReLU(q[j] . k[T_e])
+ *     dq[j]   = sum_e delta_e w[j] 1[q[j] . k[T_e] > 0] k[T_e]
+ *     dk[s]  += sum over rows and entries e with T_e = s of
+ *               delta_e sum_j w[j] 1[q[j] . k[s] > 0] q[j]
+ *
+ *   ix        the F layer's indexer inputs: BF16, dim 128, 1 <= heads <= 64
+ *             (q_scale / k_scale unused)
+ *   topk      index row length (1..2048); n_teachers = r (1..8)
+ *   idx       [batch, n_q, topk] int32 (the F layer's index tensor)
+ *   teachers  [r, batch, n_q, topk] fp32: each serving layer's teacher weight of
+ *             every index entry (0 on the padding)
+ *   loss      [batch, n_q] fp32 out (per query row)
+ *   delta     [batch, n_q, topk] fp32 out (0 on entries that take no part)
+ *   dq        [batch, n_q, heads, 128] fp32 out (16-byte aligned)
+ *   dw        [batch, n_q, heads] fp32 out
+ *   dk        [batch, n_k, 128] fp32 out (dense): overwritten -- cleared, then
+ *             accumulated with float atomics, so its summation order (and its
+ *             last bits) varies from call to call
+ * No workspace.
+ */
+typedef struct dsa_distill_args {
+  dsa_indexer_args ix;
+  int32_t topk, n_teachers;
+  const int32_t* idx;
+  const float* teachers;
+  float* loss;
+  float* delta;
+  float* dq;
+  float* dw;
+  float* dk;
+} dsa_distill_args;
+
+dsa_status dsa_indexer_distill(const dsa_distill_args* args, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -165,6 +165,18 @@ def random_sorted_indices(*, B=1, n_q, topk, q_pos0=0, n_k=None, seed=0, device=
     return idx.to(torch.int32).contiguous()
 
 
+def teacher_weights(idx: torch.Tensor, *, r: int, seed=0, device="cpu"):
+    """Synthetic teacher distributions for the distillation loss: r random
+    probability vectors per index row, [r, B, n_q, topk] fp32, over the row's
+    entries that hold a position (>= 0); zero on the -1 padding.  Weights are
+    U(0,1)^4 (a few entries carry most of the mass, as attention does),
+    normalised per row."""
+    g = generator(seed, device)
+    u = torch.rand((r,) + tuple(idx.shape), generator=g, device=device) ** 4
+    u = u * (idx >= 0).to(u.dtype).unsqueeze(0)
+    return (u / u.sum(dim=-1, keepdim=True).clamp(min=1e-30)).contiguous()
+
+
 def uniform_pattern(n_layers: int, r: int) -> str:
     """Keep every r-th indexer (F), share the rest (S): FSSSFSSS... for r=4."""
     return "".join("F" if i % r == 0 else "S" for i in range(n_layers))

@@ -168,3 +168,28 @@ def test_overlap_rejects():
     assert L.dsa_index_overlap(None, FAKE, 4, 16, FAKE, None, None) == 1
     assert L.dsa_index_overlap(FAKE, FAKE, 4, 16, None, None, None) == 1
     assert L.dsa_index_overlap(FAKE, FAKE, -1, 16, FAKE, None, None) == 1
+
+
+def distill_status(**kw):
+    d = L.DistillArgs()
+    d.ix = ix(**{k: v for k, v in kw.items() if k in ("dtype", "dim", "heads", "q", "w")})
+    d.topk, d.n_teachers = kw.get("topk", 64), kw.get("n_teachers", 2)
+    for name in ("idx", "teachers", "loss", "delta", "dq", "dw", "dk"):
+        setattr(d, name, kw.get(name, FAKE))
+    return L.dsa_indexer_distill(ctypes.byref(d), None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(topk=0), 1), (dict(topk=2049), 1), (dict(n_teachers=0), 1), (dict(n_teachers=9), 1),
+    (dict(teachers=None), 1), (dict(dk=None), 1), (dict(delta=None), 1),
+    (dict(dq=FAKE + 4), 1),                                # dq needs 16-byte alignment
+    (dict(dim=64), 2), (dict(dtype=L.DSA_FP8_E4M3), 1),    # fp8 without scales fails data checks first
+    (dict(dtype=L.DSA_F32, dim=128), 2),
+])
+def test_distill_rejects(kw, expect):
+    assert distill_status(**kw) == expect
+    assert L.dsa_last_error() != b""
+
+
+def test_distill_null_args():
+    assert L.dsa_indexer_distill(None, None) == 1
