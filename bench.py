@@ -45,6 +45,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-report", action="store_true", help="skip the all-F comparison and overlap matrix")
+    p.add_argument("--distill", action="store_true",
+                   help="training-aware IndexCache instead of the bench line: the distillation loss over "
+                        "the selected Top-k and its backward at L=16384 (H=64, d=128, k=2048, 4 teachers); "
+                        "prints one JSON object")
     p.add_argument("--sweep", action="store_true",
                    help="retention sweep instead of the bench line: both stacks under all-F, uniform 1/2, 1/4, "
                         "1/8 and (decode) the searched 47-layer patterns; prints one JSON object")
@@ -194,6 +198,64 @@ def profile_run(args, dev):
         print(f"profile indexer: fused indexer+Top-k L={L} launch {i + 1}/3 done", flush=True)
 
 
+def distill_run(args, dev):
+    """Distillation loss + backward over one F layer's index tensor: kernel time
+    with HIP events on the launch stream, algorithmic work per (query, selected
+    entry) pair, and the oracle timed on a sample of rows."""
+    import numpy as np
+    import oracle
+    import dsa_lightning_indexer_amd as dsa
+    from synth import inputs as syn
+    from threadpoolctl import threadpool_info
+    L, topk, r, H, d = 16384, 2048, 4, 64, 128
+    ix = syn.indexer_inputs(B=1, n_q=L, H=H, d=d, dtype=syn.BF16, values="normal", w_dist="u8", seed=2,
+                            device=dev)
+    idx = syn.random_sorted_indices(B=1, n_q=L, topk=topk, seed=3, device=dev)
+    T = syn.teacher_weights(idx, r=r, seed=4, device=dev)
+    pairs = int((idx >= 0).sum().item())
+    for _ in range(2):
+        dsa.indexer_distill(ix.q, ix.k, ix.w, idx, T)
+    torch.cuda.synchronize()
+    ts = time_launches(lambda: dsa.indexer_distill(ix.q, ix.k, ix.w, idx, T), max(args.kernel_reps, 3))
+    ms = sum(ts) / len(ts)
+    flop_alg = pairs * 3 * 2 * H * d                  # scores, dq, dk: one contraction over d each
+    flop_done = pairs * 7 * 2 * H * d                 # + the pass-2 score recompute (two layouts) + hi/lo halves
+    log(f"distillation L={L} k={topk} r={r}: {ms:.3f} ms, {pairs / (ms * 1e-3):.4g} pairs/s")
+    # the oracle on a bounded sample of rows
+    threads = max([dd.get("num_threads", 1) for dd in threadpool_info()] + [1])
+    qraw = ix.q[0].detach().cpu().view(torch.int16).numpy().view(np.uint16)
+    k64 = oracle.dequantize(ix.k[0].detach().cpu().view(torch.int16).numpy().view(np.uint16), "bf16")
+    w64 = ix.w[0].detach().cpu().double().numpy()
+    idx_np = idx[0].cpu().numpy()
+    T_np = T[:, 0].cpu().double().numpy()
+    rng = np.random.default_rng(0)
+    done = rows = 0
+    t0 = time.perf_counter()
+    for i in rng.permutation(L):
+        q64 = oracle.dequantize(qraw[i:i + 1], "bf16")
+        oracle.indexer_distill(q64, k64, w64[i:i + 1], idx_np[i:i + 1], T_np[:, i:i + 1], q_pos0=int(i))
+        done += int((idx_np[i] >= 0).sum())
+        rows += 1
+        if time.perf_counter() - t0 >= args.cpu_seconds:
+            break
+    dt = time.perf_counter() - t0
+    rec = {
+        "metric": "distillation loss + backward, (query, selected entry) pairs/s",
+        "value": pairs / (ms * 1e-3), "unit": "pairs/s", "n_gpus": 1, "higher_is_better": True,
+        "ms_per_call": ms, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"one F layer: L={L} queries, H={H}, d={d}, k={topk} selected entries per row, "
+                               f"{r} teacher distributions", "pairs": pairs},
+        "roofline": {"bound": "mfma", "achieved": flop_alg / (ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": flop_alg / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                     "algorithmic_per_call": f"{pairs} pairs x 3 x {2 * H * d} flop = {flop_alg:.4g} flop",
+                     "executed_mfma_flop": f"{flop_done:.4g}",
+                     "key_bytes_gathered": pairs * d * 2 * 2, "dk_float_atomics": pairs * d},
+        "cpu_baseline": {"value": done / dt, "unit": "pairs/s", "cores": int(threads), "kind": "oracle",
+                         "sample": f"{rows} random rows, {done} pairs in {dt:.1f} s, float64 NumPy"},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def sweep_run(args, dev):
     """Stack time per sharing pattern (same kernels and driver as the bench line)."""
     import dsa_lightning_indexer_amd as dsa
@@ -293,6 +355,9 @@ def main():
         return
     if args.sweep:
         sweep_run(args, dev)
+        return
+    if args.distill:
+        distill_run(args, dev)
         return
     import dsa_lightning_indexer_amd as dsa
     from synth import inputs as syn

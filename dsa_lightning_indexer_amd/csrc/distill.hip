@@ -16,9 +16,9 @@
 //     D^T = K . q^T  (16 keys x 16 heads; lane = head, 4 keys in registers)
 // with v_mfma_f32_16x16x32_bf16 over the 128-wide rows (4 K steps).
 //   pass 1: z_e = sum_j w_j ReLU(D_je): four in-lane FMAs and a lane-swap sum
-//           over the wave's four head groups give each wave's partial, stored
-//           per wave and summed in a fixed order (loss, delta, dq and dw do not
-//           depend on the order the waves run in).
+//           over the wave's four head groups give each wave's partial; after the
+//           next step's barrier wave 0 sums the four partials in a fixed order
+//           (loss, delta, dq and dw do not depend on the order the waves run in).
 //   softmax over the row's valid entries, the loss against the r teachers and
 //           delta_e = pi_e * sum(p_bar) - p_bar_e (LDS, block reductions).
 //   pass 2: G_je = delta_e w_j 1[D_je > 0] in both layouts (bf16 hi + lo parts,
@@ -26,11 +26,14 @@
 //           dq^T += K^T . G^T  (v_mfma_f32_16x16x16bf16_1k; K^T from a
 //                               transposing LDS read of the key tile, G^T is
 //                               the D^T accumulator layout as it stands)
-//           dk    = G . q      (G in the D layout is the A operand as it
-//                               stands); the four waves' partial tiles meet in
-//                               LDS (float adds), then one global float atomic
+//           dk    = G . q      (each wave writes its heads' G, in the D layout,
+//                               to an LDS tile of all 64 heads; one step later,
+//                               after the next barrier, wave w forms dk for
+//                               columns [32w, 32w+32) over every head -- G in
+//                               the D layout is the A operand as it stands --
+//                               and adds it to dk with one global float atomic
 //                               per (key, dim): dk accumulates over query rows
-//                               in an order that varies between calls
+//                               in an order that varies between calls)
 //           dw_j += sum_e delta_e ReLU(D_je).
 #include "common.hpp"
 
@@ -105,12 +108,12 @@ __device__ float block_max(float v, float* sh) {
   return r;
 }
 
-__global__ __launch_bounds__(256, 2) void distill_kernel(DistillParams p) {
+__global__ __launch_bounds__(256, 4) void distill_kernel(DistillParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[2][kKeys * kPitch];
-  // pass 1: the waves' partial scores [4][topk]; pass 2: the key-gradient tile of
-  // two consecutive steps [2][16 x 128], summed over the waves
-  __shared__ __attribute__((aligned(16))) float scr[4 * kMaxTopk];
-  __shared__ __attribute__((aligned(16))) float zd[kMaxTopk];   // delta per index entry
+  __shared__ float zpart[2][4][kKeys];        // the waves' partial scores of two steps (pass 1)
+  // G of two consecutive steps (pass 2): [2][hi, lo][16 keys][64 heads] bf16
+  __shared__ __attribute__((aligned(16))) __bf16 gx[2][2][kKeys * 64];
+  __shared__ __attribute__((aligned(16))) float zd[kMaxTopk];   // z, then delta, per index entry
   __shared__ int32_t sidx[kMaxTopk];          // the row's index entries (-1 where nothing is selected)
   __shared__ float red[8];
 
@@ -138,14 +141,18 @@ __global__ __launch_bounds__(256, 2) void distill_kernel(DistillParams p) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[ks] = hv ? *(const bf16x8*)(qr + 32 * ks + 8 * g) : bf16x8{};
   }
-  // q as the B operand of G . q: lane holds column 16 nt + col, heads h0 + 4 g .. + 4
-  bf16x4 qb[8];
+  // q as the B operand of G . q for this wave's columns: lane holds column
+  // 32 w + 16 nt + col, heads 16 kk + 4 g .. + 4
+  bf16x4 qb[4][2];
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
+  for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = h0 + 4 * g + i;
-      qb[nt][i] = h < p.heads ? p.q[((gi * p.heads) + h) * (int64_t)kD + 16 * nt + col] : (__bf16)0.f;
+    for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = 16 * kk + 4 * g + i;
+        qb[kk][nt][i] = h < p.heads ? p.q[((gi * p.heads) + h) * (int64_t)kD + 32 * w + 16 * nt + col] : (__bf16)0.f;
+      }
     }
   }
   // head weights: wc for the D^T layout (head h0+col), wr[i] for the D layout (heads h0+4g+i)
@@ -176,9 +183,17 @@ __global__ __launch_bounds__(256, 2) void distill_kernel(DistillParams p) {
     i32x4 nxt = gload(0);
     gstore(0, nxt);
     nxt = gload(1);
+    // z of step st from the four partials (fixed order), after the next barrier
+    auto zsum = [&](int st) {
+      if (w == 0 && lane < kKeys) {
+        const float* zp = &zpart[st & 1][0][0];
+        zd[st * kKeys + lane] = ((zp[lane] + zp[kKeys + lane]) + zp[2 * kKeys + lane]) + zp[3 * kKeys + lane];
+      }
+    };
     for (int st = 0; st < nsteps; ++st) {
       sync_lds_barrier();
       const int buf = st & 1;
+      if (st > 0) zsum(st - 1);
       if (st + 1 < nsteps) gstore(buf ^ 1, nxt);
       if (st + 2 < nsteps) nxt = gload(st + 2);
       f32x4 d = f32x4{};
@@ -189,8 +204,10 @@ __global__ __launch_bounds__(256, 2) void distill_kernel(DistillParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) zp = fmaf(wr[i], fmaxf(d[i], 0.f), zp);
       zp = quad_sum(zp);
-      if (g == 0) scr[w * kMaxTopk + st * kKeys + col] = zp;
+      if (g == 0) zpart[st & 1][w][col] = zp;
     }
+    sync_lds_barrier();
+    zsum(nsteps - 1);
   }
   __syncthreads();
 
@@ -201,9 +218,7 @@ __global__ __launch_bounds__(256, 2) void distill_kernel(DistillParams p) {
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int e = threadIdx.x + 256 * j;
-    zv[j] = (e < topk && sidx[e] >= 0)
-                ? ((scr[e] + scr[kMaxTopk + e]) + scr[2 * kMaxTopk + e]) + scr[3 * kMaxTopk + e]
-                : -__builtin_inff();
+    zv[j] = (e < topk && sidx[e] >= 0) ? zd[e] : -__builtin_inff();
     mx = fmaxf(mx, zv[j]);
   }
   mx = block_max(mx, red);
@@ -240,9 +255,6 @@ __global__ __launch_bounds__(256, 2) void distill_kernel(DistillParams p) {
     if (e < topk) p.delta[gi * topk + e] = dl;
   }
   __syncthreads();
-  float* dkt = scr;                            // [2][16 x 128] from here on
-  for (int i = threadIdx.x; i < 2 * kKeys * kD; i += 256) dkt[i] = 0.f;
-  __syncthreads();
 
   // ---------------- pass 2: dq, dw, dk
   f32x4 dqa[8];
@@ -251,6 +263,31 @@ __global__ __launch_bounds__(256, 2) void distill_kernel(DistillParams p) {
   float dwa = 0.f;
   float* dkb = p.dk + (int64_t)b * p.n_k * kD;
   const uint8_t* rb = nullptr;
+  // dk rows of step st from the G tile in gx[st & 1]: wave w, columns 32 w ..;
+  // lane (g, col): column 32 w + 16 nt + col, keys 4 g .. 4 g + 3
+  auto dk_step = [&](int st) {
+    const __bf16* gh = gx[st & 1][0];
+    const __bf16* gl = gx[st & 1][1];
+    f32x4 o[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x4 ah = *(const bf16x4*)(gh + col * 64 + 16 * kk + 4 * g);
+      const bf16x4 al = *(const bf16x4*)(gl + col * 64 + 16 * kk + 4 * g);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, qb[kk][nt], o[nt], 0, 0, 0);
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, qb[kk][nt], o[nt], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = sidx[st * kKeys + 4 * g + i];
+      if (s < 0) continue;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        if (o[nt][i] != 0.f) atomicAdd(&dkb[(int64_t)s * kD + 32 * w + 16 * nt + col], o[nt][i]);
+    }
+  };
   {
     i32x4 nxt = gload(0);
     gstore(0, nxt);
@@ -258,18 +295,8 @@ __global__ __launch_bounds__(256, 2) void distill_kernel(DistillParams p) {
     for (int st = 0; st < nsteps; ++st) {
       sync_lds_barrier();
       const int buf = st & 1;
-      // the previous step's key-gradient tile is complete: add it to dk, clear it
-      if (st > 0) {
-        float* tl = dkt + (buf ^ 1) * kKeys * kD;
-        const int s = sidx[(st - 1) * kKeys + trow];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const int dcol = tch + 16 * c;
-          const float v = tl[trow * kD + dcol];
-          if (s >= 0 && v != 0.f) atomicAdd(&dkb[(int64_t)s * kD + dcol], v);
-          tl[trow * kD + dcol] = 0.f;
-        }
-      }
+      // every wave's G of the previous step is in LDS now
+      if (st > 0) dk_step(st - 1);
       if (st + 1 < nsteps) gstore(buf ^ 1, nxt);
       if (st + 2 < nsteps) nxt = gload(st + 2);
       f32x4 d = f32x4{}, dt = f32x4{};
@@ -282,7 +309,7 @@ __global__ __launch_bounds__(256, 2) void distill_kernel(DistillParams p) {
       const int e0 = st * kKeys;
       const f32x4 dl4 = *(const f32x4*)&zd[e0 + 4 * g];   // delta of keys 4g .. 4g+3
       const float dlc = zd[e0 + col];                      // delta of key col
-      // G^T (lane = head col): delta_key * w_head * 1[D > 0]; dw partial
+      // G^T (lane = head col) and G (lane = key col): delta_key * w_head * 1[D > 0]; dw partial
       float gt[4], gk[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -293,6 +320,9 @@ __global__ __launch_bounds__(256, 2) void distill_kernel(DistillParams p) {
       bf16x4 gth, gtl, gkh, gkl;
       split4(gt, gth, gtl);
       split4(gk, gkh, gkl);
+      // G rows for the dk step: key col, heads h0 + 4 g .. + 4
+      *(bf16x4*)(gx[buf][0] + col * 64 + h0 + 4 * g) = gkh;
+      *(bf16x4*)(gx[buf][1] + col * 64 + h0 + 4 * g) = gkl;
       // dq^T[16 nt + col-row][head] += K^T . G^T
       rb = tile[buf] + (4 * g + (col >> 2)) * kPitch + 8 * (col & 3);
 #pragma unroll
@@ -301,28 +331,9 @@ __global__ __launch_bounds__(256, 2) void distill_kernel(DistillParams p) {
         dqa[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, gth, dqa[nt], 0, 0, 0);
         dqa[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, gtl, dqa[nt], 0, 0, 0);
       }
-      // dk partial [16 keys x 128 dims] = G . q over this wave's heads -> LDS
-      float* tl = dkt + buf * kKeys * kD;
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        f32x4 o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(gkh, qb[nt], f32x4{}, 0, 0, 0);
-        o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(gkl, qb[nt], o, 0, 0, 0);
-        // lane (g, col): dim 16 nt + col, keys 4g + i
-#pragma unroll
-        for (int i = 0; i < 4; ++i) atomicAdd(&tl[(4 * g + i) * kD + 16 * nt + col], o[i]);
-      }
     }
     sync_lds_barrier();
-    {
-      float* tl = dkt + ((nsteps - 1) & 1) * kKeys * kD;
-      const int s = sidx[(nsteps - 1) * kKeys + trow];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int dcol = tch + 16 * c;
-        const float v = tl[trow * kD + dcol];
-        if (s >= 0 && v != 0.f) atomicAdd(&dkb[(int64_t)s * kD + dcol], v);
-      }
-    }
+    dk_step(nsteps - 1);
   }
   // dq^T layout: lane (g, col): head h0 + col, dims 16 nt + 4 g + i
   if (hv) {
