@@ -249,7 +249,8 @@ def distill_run(args, dev):
                      "unit": "TFLOP/s", "frac": flop_alg / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                      "algorithmic_per_call": f"{pairs} pairs x 3 x {2 * H * d} flop = {flop_alg:.4g} flop",
                      "executed_mfma_flop": f"{flop_done:.4g}",
-                     "key_bytes_gathered": pairs * d * 2 * 2, "dk_float_atomics": pairs * d},
+                     "key_bytes_gathered": pairs * d * 2 * 2, "dk_float_atomics": pairs * d,
+                     "dk_float_atomics_per_s": pairs * d / (ms * 1e-3)},
         "cpu_baseline": {"value": done / dt, "unit": "pairs/s", "cores": int(threads), "kind": "oracle",
                          "sample": f"{rows} random rows, {done} pairs in {dt:.1f} s, float64 NumPy"},
     }
