@@ -13,7 +13,8 @@ Plain, slow, float64 NumPy.  Sources (web pages, cited by title and section):
 
 Parity pins: every function here is pinned by the CPU test suite against
 worked examples printed on those pages, closed forms, library routines or
-invariants -- see tests/test_oracle_pins.py and tests/test_oracle_distill_pins.py.
+invariants -- see tests/test_oracle_pins.py, tests/test_oracle_distill_pins.py and
+tests/test_oracle_pattern_pins.py.
 No function is unpinned.
 """
 from .numerics import bf16_bits_to_f64, e4m3fn_codes_to_f64, dequantize  # noqa: F401
@@ -22,3 +23,6 @@ from .dsa import (  # noqa: F401
     indexcache_forward, overlap, overlap_matrix, amdahl_speedup,
 )
 from .distill import kl_multi, kl_average, indexer_distill  # noqa: F401
+from .pattern_search import (  # noqa: F401
+    row_cosine, output_similarity, similarity_matrix, pattern_objective, pattern_search_brute,
+)
