@@ -52,6 +52,12 @@ def parse():
     p.add_argument("--sweep", action="store_true",
                    help="retention sweep instead of the bench line: both stacks under all-F, uniform 1/2, 1/4, "
                         "1/8 and (decode) the searched 47-layer patterns; prints one JSON object")
+    p.add_argument("--similarity", action="store_true",
+                   help="similarity-based pattern search instead of the bench line: the similarity matrix "
+                        "of a 47-layer calibration prefill (L=--similarity-len, drifting indexer keys) and "
+                        "the dynamic-program patterns at 24/12/7 F layers; prints one JSON object")
+    p.add_argument("--similarity-len", type=int, default=16384)
+    p.add_argument("--similarity-layers", type=int, default=47)
     p.add_argument("--profile", choices=["indexer", "attn", "copy"], default=None,
                    help="counter-collection runs: 'indexer' launches only the prefill F layer's fused "
                         "indexer+Top-k (3 launches, the first a warm-up); 'attn' that layer's prefill "
@@ -257,6 +263,105 @@ def distill_run(args, dev):
     print(json.dumps(rec), flush=True)
 
 
+def similarity_run(args, dev):
+    """Similarity matrix + pattern search ([IC-SUMMARY] Appendix C) on a drifting
+    calibration stack: whole-matrix time with HIP events, the per-kernel
+    durations of its attention and cosine launches, the host dynamic program,
+    and the oracle timed on a sample of rows of one matrix entry."""
+    import numpy as np
+    import oracle
+    from oracle import pattern_search as ps
+    import dsa_lightning_indexer_amd as dsa
+    from synth import inputs as syn
+    from threadpoolctl import threadpool_info
+    L, n, topk = args.similarity_len, args.similarity_layers, 2048
+    layers, jumps = syn.drift_stack(n_layers=n, n_q=L, seed=6, device=dev)
+    ixs = [dict(q=ix.q, k=ix.k, w=ix.w) for ix, _ in layers]
+    sas = [dict(q=sa.q, kv=sa.kv, scale=sa.scale, d_v=sa.d_v) for _, sa in layers]
+    idx = [torch.empty((1, L, topk), dtype=torch.int32, device=dev) for _ in range(n)]
+    ws = torch.empty(dsa.similarity_matrix_workspace_size(ixs, sas, topk), dtype=torch.uint8, device=dev)
+    for _ in range(max(args.warmup, 1)):
+        S, _ = dsa.similarity_matrix(ixs, sas, topk, idx_out=idx, ws=ws)
+    torch.cuda.synchronize()
+    ts = time_launches(lambda: dsa.similarity_matrix(ixs, sas, topk, idx_out=idx, ws=ws), max(args.steps, 1))
+    ms = sum(ts) / len(ts)
+    S, _ = dsa.similarity_matrix(ixs, sas, topk, idx_out=idx, ws=ws)
+    Sh = S.cpu().numpy()
+    # per-kernel durations of the launches the matrix is made of
+    sa = layers[1][1]
+    o_own = dsa.sparse_attn(sa.q, sa.kv, idx[1], sa.scale, d_v=sa.d_v)
+    o_re = torch.empty_like(o_own)
+    reps = max(args.kernel_reps, 3)
+    t_sa = time_launches(lambda: dsa.sparse_attn(sa.q, sa.kv, idx[0], sa.scale, d_v=sa.d_v, out=o_re), reps)
+    t_cos = time_launches(lambda: dsa.row_cosine(o_own.reshape(L, -1), o_re.reshape(L, -1)), reps)
+    sa_ms, cos_ms = sum(t_sa) / len(t_sa), sum(t_cos) / len(t_cos)
+    sel = int((idx[0] >= 0).sum().item())
+    gather = sel * 576 * 2
+    cos_bytes = 2 * o_own.numel() * 4
+    pairs = n * (n - 1) // 2
+    # dynamic program at the printed retention counts
+    pats = {}
+    for m in (24, 12, 7):
+        t0 = time.perf_counter()
+        pat, score = dsa.pattern_search(Sh, m)
+        dp_us = (time.perf_counter() - t0) * 1e6
+        r = {24: 2, 12: 4, 7: 8}[m]
+        uni = "".join("F" if i % r == 0 else "S" for i in range(n))
+        pats[str(m)] = {"pattern": pat, "score": score, "dp_us": dp_us,
+                        "uniform_1/%d" % r: {"pattern": uni, "F": uni.count("F"),
+                                             "score": ps.pattern_objective(Sh, uni)}}
+    log(f"similarity matrix {n} layers L={L}: {ms:.1f} ms; attention {sa_ms:.3f} ms, cosine {cos_ms * 1e3:.1f} us")
+    # the oracle: one matrix entry (layer 1 vs layer 0) on a bounded sample of rows
+    threads = max([dd.get("num_threads", 1) for dd in threadpool_info()] + [1])
+
+    def f64(t):
+        return oracle.dequantize(t.detach().cpu().view(torch.int16).numpy().view(np.uint16), "bf16")
+    ix0, ix1 = layers[0][0], layers[1][0]
+    k0, k1 = f64(ix0.k[0]), f64(ix1.k[0])
+    w64 = ix0.w[0].detach().cpu().double().numpy()
+    KV = f64(sa.kv[0])
+    rng = np.random.default_rng(0)
+    rows = 0
+    t0 = time.perf_counter()
+    for i in rng.permutation(L):
+        q64 = f64(ix0.q[0, i:i + 1])
+        T0, _, _ = oracle.indexer_topk(q64, k0, w64[i:i + 1], topk, q_pos0=int(i))
+        T1, _, _ = oracle.indexer_topk(q64, k1, w64[i:i + 1], topk, q_pos0=int(i))
+        Q = f64(sa.q[0, i:i + 1])
+        own = oracle.sparse_attn(Q, KV, KV[..., :sa.d_v], T1, sa.scale)
+        other = oracle.sparse_attn(Q, KV, KV[..., :sa.d_v], T0, sa.scale)
+        ps.row_cosine(own, other)
+        rows += 1
+        if time.perf_counter() - t0 >= args.cpu_seconds:
+            break
+    dt = time.perf_counter() - t0
+    rec = {
+        "metric": "similarity-matrix (calibration row, layer pair) entries/s",
+        "value": L * pairs / (ms * 1e-3), "unit": "row-pairs/s", "n_gpus": 1, "higher_is_better": True,
+        "ms_per_matrix": ms, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{n}-layer calibration prefill L={L} (drifting bf16 indexer keys, 64 heads x 128, "
+                               f"k={topk}; 16-head MLA attention 576/512)", "layer_pairs": pairs,
+                   "jump_layers": [l for l, j in enumerate(jumps) if j]},
+        "kernels": {"sparse_attn_ms": sa_ms, "sparse_attn_gathered_TBps": gather / (sa_ms * 1e-3) / 1e12,
+                    "row_cosine_us": cos_ms * 1e3, "row_cosine_GBps": cos_bytes / (cos_ms * 1e-3) / 1e9,
+                    "launches_per_matrix": {"topk": n, "sparse_attn": n - 1 + pairs, "row_cosine+mean": pairs}},
+        "roofline": {"bound": "hbm", "kernel": "sa_mla4_kernel (one layer pair)",
+                     "achieved": gather / (sa_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gather / (sa_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "algorithmic_per_launch": f"{sel} selected (row, position) pairs x 1152 B = {gather:.4g} B",
+                     "traffic": None},
+        "row_cosine_roofline": {"bound": "hbm", "achieved": cos_bytes / (cos_ms * 1e-3) / 1e9,
+                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": cos_bytes / (cos_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                "algorithmic_per_launch": f"2 x {L} rows x {o_own[0].numel()} fp32 = {cos_bytes} B"},
+        "patterns": pats,
+        "cpu_baseline": {"value": rows / dt, "unit": "row-pairs/s", "cores": int(threads), "kind": "oracle",
+                         "sample": f"{rows} random rows of entry S[1, 0] (both layers' indexer + Top-k, two "
+                                   f"attention rows, one cosine) in {dt:.1f} s, float64 NumPy"},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def sweep_run(args, dev):
     """Stack time per sharing pattern (same kernels and driver as the bench line)."""
     import dsa_lightning_indexer_amd as dsa
@@ -359,6 +464,9 @@ def main():
         return
     if args.distill:
         distill_run(args, dev)
+        return
+    if args.similarity:
+        similarity_run(args, dev)
         return
     import dsa_lightning_indexer_amd as dsa
     from synth import inputs as syn

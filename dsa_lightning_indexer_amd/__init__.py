@@ -11,4 +11,5 @@ from ._lib import (  # noqa: F401
 from .api import (  # noqa: F401
     indexer_scores, topk, topk_workspace_size, sparse_attn, sparse_attn_workspace_size,
     indexcache_forward, indexcache_forward_workspace_size, index_overlap, indexer_distill,
+    row_cosine, similarity_matrix, similarity_matrix_workspace_size, pattern_search,
 )

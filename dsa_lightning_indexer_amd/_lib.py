@@ -71,11 +71,17 @@ indexcache_forward_c = _sig("indexcache_forward", c_i32, ctypes.c_char_p, c_i32,
                             ctypes.POINTER(c_i32), c_vp, c_sz, c_vp)
 dsa_index_overlap = _sig("dsa_index_overlap", c_i32, c_vp, c_vp, c_i64, c_i32, c_vp, c_vp, c_vp)
 dsa_indexer_distill = _sig("dsa_indexer_distill", c_i32, ctypes.POINTER(DistillArgs), c_vp)
+dsa_row_cosine = _sig("dsa_row_cosine", c_i32, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp)
+dsa_similarity_matrix_workspace_size = _sig("dsa_similarity_matrix_workspace_size", c_sz, c_i32, P_LAYER, c_i32)
+dsa_similarity_matrix = _sig("dsa_similarity_matrix", c_i32, c_i32, P_LAYER, c_i32, c_vp, c_vp, c_sz, c_vp)
+dsa_pattern_search = _sig("dsa_pattern_search", c_i32, ctypes.POINTER(ctypes.c_double), c_i32, c_i32,
+                          ctypes.c_char_p, ctypes.POINTER(ctypes.c_double))
 
 EXPORTS = ["dsa_abi_version", "dsa_status_string", "dsa_last_error", "dsa_indexer_scores",
            "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_attn_workspace_size", "dsa_sparse_attn",
            "indexcache_forward_workspace_size", "indexcache_forward", "dsa_index_overlap",
-           "dsa_indexer_distill"]
+           "dsa_indexer_distill", "dsa_row_cosine", "dsa_similarity_matrix_workspace_size",
+           "dsa_similarity_matrix", "dsa_pattern_search"]
 
 
 class DsaError(RuntimeError):

@@ -144,3 +144,73 @@ def indexer_distill(q, k, w, idx, teachers, *, q_pos0=0):
         setattr(a, name, out[name].data_ptr())
     L.check(L.dsa_indexer_distill(ctypes.byref(a), _stream()))
     return out
+
+
+def row_cosine(a, b, *, row_cos=None, mean=None):
+    """Per-row cosine similarity of two fp32 tensors (leading dim = rows, the rest
+    flattened).  Returns (row_cos fp32 [rows], mean float64 [1])."""
+    rows = a.shape[0]
+    width = a[0].numel() if rows else 0
+    if row_cos is None:
+        row_cos = torch.empty(rows, dtype=torch.float32, device=a.device)
+    if mean is None:
+        mean = torch.empty(1, dtype=torch.float64, device=a.device)
+    L.check(L.dsa_row_cosine(a.data_ptr(), b.data_ptr(), rows, width, row_cos.data_ptr(), mean.data_ptr(),
+                             _stream()))
+    return row_cos, mean
+
+
+def _all_f_layers(ix_list, sa_list, k, idx_out):
+    specs = [{"ix": ix, "sa": sa, "idx_out": io} for ix, sa, io in zip(ix_list, sa_list, idx_out)]
+    return _layers(specs, k)
+
+
+def _sim_layers(ix_list, sa_list, k, idx_out):
+    dev = sa_list[0]["q"].device
+    if any(sa.get("d_v") is None and sa.get("v") is None for sa in sa_list):
+        raise ValueError("each attention spec needs d_v (or a separate v)")
+    dummy = torch.empty(0, device=dev)
+    sas = [dict(sa, out=dummy, d_v=sa.get("d_v") or sa["v"].shape[-1]) for sa in sa_list]
+    return _all_f_layers(ix_list, sas, k, idx_out)
+
+
+def similarity_matrix_workspace_size(ix_list, sa_list, k):
+    arr = _sim_layers(ix_list, sa_list, k, [None] * len(ix_list))
+    return L.dsa_similarity_matrix_workspace_size(len(ix_list), arr, k)
+
+
+def similarity_matrix(ix_list, sa_list, k, *, idx_out=None, ws=None):
+    """Similarity matrix of the pattern search: every layer's own Top-k, then
+    S[i, j] = mean row cosine of layer i's attention output under T_i and under T_j.
+    ix_list[l]: {"q", "k", "w", optional "q_scale", "k_scale", "q_pos0"};
+    sa_list[l]: {"q", "kv", "scale", optional "v", "d_v"} ("out" is not used).
+    Returns (S float64 [N, N] on the device, [T_l int32 [B, n_q, k]])."""
+    n = len(ix_list)
+    dev = sa_list[0]["q"].device
+    B, n_q = ix_list[0]["q"].shape[:2]
+    if idx_out is None:
+        idx_out = [torch.empty((B, n_q, k), dtype=torch.int32, device=dev) for _ in range(n)]
+    arr = _sim_layers(ix_list, sa_list, k, idx_out)
+    need = L.dsa_similarity_matrix_workspace_size(n, arr, k)
+    if need == 0:
+        L.check(L.dsa_similarity_matrix(n, arr, k, None, None, 0, _stream()))   # raises with the reason
+    wbuf, wbytes = _ws(need, dev, ws)
+    S = torch.empty((n, n), dtype=torch.float64, device=dev)
+    L.check(L.dsa_similarity_matrix(n, arr, k, S.data_ptr(), wbuf.data_ptr(), wbytes, _stream()))
+    return S, idx_out
+
+
+def pattern_search(S, n_full):
+    """Sharing pattern with layer 0 F and n_full F layers maximising the total
+    similarity (host dynamic program).  S: [N, N] (numpy or torch, any device).
+    Returns (pattern str, score)."""
+    if isinstance(S, torch.Tensor):
+        S = S.detach().to("cpu", torch.float64).numpy()
+    import numpy as np
+    S = np.ascontiguousarray(S, dtype=np.float64)
+    n = S.shape[0]
+    buf = ctypes.create_string_buffer(n + 1)
+    score = ctypes.c_double()
+    L.check(L.dsa_pattern_search(S.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), n, int(n_full), buf,
+                                 ctypes.byref(score)))
+    return buf.value.decode(), score.value

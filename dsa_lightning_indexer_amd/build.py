@@ -14,7 +14,8 @@ BUILD = os.path.join(HERE, "_build")
 ARCH = os.environ.get("DSA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["select.hip", "select_few.hip", "indexer.hip", "sparse_attn.hip", "overlap.hip", "distill.hip", "api.cpp"]
+SOURCES = ["select.hip", "select_few.hip", "indexer.hip", "sparse_attn.hip", "overlap.hip", "distill.hip", "similarity.hip",
+           "pattern_search.cpp", "api.cpp"]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     # keep the compiler from emitting packed fp32 VALU ops

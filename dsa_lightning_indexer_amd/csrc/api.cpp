@@ -3,7 +3,9 @@
 // Every check runs before anything is enqueued.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -167,7 +169,7 @@ dsa_status run_topk(const dsa_indexer_args* a, const float* scores, int32_t k, i
 }
 
 // ------------------------------------------------------------------ attention args
-dsa_status check_sa(const dsa_sparse_attn_args* a, bool need_idx) {
+dsa_status check_sa(const dsa_sparse_attn_args* a, bool need_idx, bool need_out = true) {
   if (!a) return fail(DSA_ERR_INVALID, "sparse attention args is NULL");
   if (a->dtype != DSA_F32 && a->dtype != DSA_BF16)
     return fail(DSA_ERR_UNSUPPORTED, "sparse attention dtype must be F32 or BF16 (got %d)", a->dtype);
@@ -178,7 +180,7 @@ dsa_status check_sa(const dsa_sparse_attn_args* a, bool need_idx) {
     return fail(DSA_ERR_UNSUPPORTED, "d_qk and d_v must be 1..1024");
   if (!a->v && a->d_v > a->d_qk) return fail(DSA_ERR_INVALID, "latent V needs d_v <= d_qk");
   if (a->topk < 1 || a->topk > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID, "topk must be 1..%d", DSA_MAX_TOPK);
-  if (!a->q || !a->kv || !a->out || (need_idx && !a->idx))
+  if (!a->q || !a->kv || (need_out && !a->out) || (need_idx && !a->idx))
     return fail(DSA_ERR_INVALID, "sparse attention q, kv, idx and out must be non-NULL");
   if (!(a->scale == a->scale)) return fail(DSA_ERR_INVALID, "scale is NaN");
   const int64_t row = (int64_t)a->kv_heads * a->d_qk;
@@ -187,7 +189,7 @@ dsa_status check_sa(const dsa_sparse_attn_args* a, bool need_idx) {
   if (a->v && a->v_batch_stride != 0 && a->v_batch_stride < (int64_t)a->n_k * a->kv_heads * a->d_v)
     return fail(DSA_ERR_INVALID, "v_batch_stride too small");
   const size_t al = a->dtype == DSA_BF16 ? 16 : 4;
-  if (!aligned(a->q, al) || !aligned(a->kv, al) || !aligned(a->out, 4) ||
+  if (!aligned(a->q, al) || !aligned(a->kv, al) || (a->out && !aligned(a->out, 4)) ||
       (a->idx && !aligned(a->idx, 4)) || (a->v && !aligned(a->v, 4)))
     return fail(DSA_ERR_INVALID, "sparse attention pointers misaligned");
   if (a->dtype == DSA_BF16 && a->kv_batch_stride % 8 != 0)
@@ -363,6 +365,123 @@ dsa_status dsa_index_overlap(const int32_t* a, const int32_t* b, int64_t rows, i
   if (rows > 0 && (!a || !b)) return fail(DSA_ERR_INVALID, "index tensors must be non-NULL");
   if (!row_counts && !total) return fail(DSA_ERR_INVALID, "need row_counts and/or total");
   return hip_status(dsa_host::overlap_launch(a, b, rows, k, row_counts, total, stream), "overlap launch");
+}
+
+dsa_status dsa_row_cosine(const float* a, const float* b, int64_t rows, int64_t width, float* row_cos,
+                          double* mean, hipStream_t stream) {
+  g_last_error.clear();
+  if (rows < 1 || rows > INT32_MAX) return fail(DSA_ERR_INVALID, "rows must be 1..2^31-1");
+  if (width < 4 || width > ((int64_t)1 << 26) || width % 4 != 0)
+    return fail(DSA_ERR_INVALID, "width must be a multiple of 4 in [4, 2^26]");
+  if (!a || !b || !row_cos) return fail(DSA_ERR_INVALID, "a, b and row_cos are required");
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(row_cos, 4) || (mean && !aligned(mean, 8)))
+    return fail(DSA_ERR_INVALID, "a and b must be 16-byte aligned, row_cos 4, mean 8");
+  return hip_status(dsa_host::row_cosine_launch(a, b, rows, width, row_cos, mean, stream), "cosine launch");
+}
+
+// Workspace: O_own and O_other (fp32 [rows, heads * d_v] each, sized for the
+// widest layer), the per-row cosines, then the Top-k / attention workspace
+// (the calls run one after another on the stream and share it).
+struct SimLayout {
+  size_t out_bytes, cos_bytes, tail_bytes, total;
+};
+
+// sizing: only shapes matter (the index tensors need not exist yet).
+static dsa_status check_similarity(int32_t n, const dsa_layer* layers, int32_t k, SimLayout* lay, bool sizing) {
+  if (n < 1 || n > 1024) return fail(DSA_ERR_INVALID, "n_layers must be 1..1024");
+  if (!layers) return fail(DSA_ERR_INVALID, "layers is NULL");
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID, "k must be 1..%d", DSA_MAX_TOPK);
+  size_t width = 0, tail = 0;
+  const int64_t rows = (int64_t)layers[0].ix.batch * layers[0].ix.n_q;
+  for (int32_t l = 0; l < n; ++l) {
+    const dsa_layer& L = layers[l];
+    dsa_status st = check_indexer_shape(&L.ix);
+    if (st == DSA_OK) st = check_indexer_data(&L.ix);
+    if (st != DSA_OK) return fail(st, "layer %d: %s", l, g_last_error.c_str());
+    if (!sizing && (!L.idx_out || !aligned(L.idx_out, 4)))
+      return fail(DSA_ERR_INVALID, "layer %d: idx_out NULL/misaligned", l);
+    st = check_sa(&L.sa, false, false);   // sa.idx and sa.out are not used
+    if (st != DSA_OK) return fail(st, "layer %d: %s", l, g_last_error.c_str());
+    if (L.ix.batch != layers[0].ix.batch || L.ix.n_q != layers[0].ix.n_q || L.sa.batch != L.ix.batch ||
+        L.sa.n_q != L.ix.n_q || L.sa.topk != k)
+      return fail(DSA_ERR_INVALID, "layer %d: indexer and attention batch/n_q must match layer 0's and "
+                  "sa.topk must equal k", l);
+    const int64_t w = (int64_t)L.sa.heads * L.sa.d_v;
+    if (w % 4 != 0) return fail(DSA_ERR_UNSUPPORTED, "layer %d: heads * d_v must be a multiple of 4", l);
+    if ((size_t)w > width) width = (size_t)w;
+    const size_t t1 = topk_ws(&L.ix, nullptr);
+    const size_t t2 = align_up(dsa_host::sparse_attn_ws_bytes(L.sa));
+    if (t1 > tail) tail = t1;
+    if (t2 > tail) tail = t2;
+  }
+  lay->out_bytes = align_up((size_t)rows * width * sizeof(float));
+  lay->cos_bytes = align_up((size_t)rows * sizeof(float));
+  lay->tail_bytes = tail;
+  lay->total = 2 * lay->out_bytes + lay->cos_bytes + tail;
+  return DSA_OK;
+}
+
+size_t dsa_similarity_matrix_workspace_size(int32_t n, const dsa_layer* layers, int32_t k) {
+  SimLayout lay{};
+  if (check_similarity(n, layers, k, &lay, true) != DSA_OK) return 0;
+  return lay.total;
+}
+
+dsa_status dsa_similarity_matrix(int32_t n, const dsa_layer* layers, int32_t k, double* S, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  SimLayout lay{};
+  dsa_status st = check_similarity(n, layers, k, &lay, false);
+  if (st != DSA_OK) return st;
+  if (!S || !aligned(S, 8)) return fail(DSA_ERR_INVALID, "S must be non-NULL and 8-byte aligned");
+  if (!ws || ws_bytes < lay.total)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total, ws ? ws_bytes : 0);
+  if (!aligned(ws, kAlign)) return fail(DSA_ERR_INVALID, "workspace must be 256-byte aligned");
+  uint8_t* base = (uint8_t*)ws;
+  float* o_own = (float*)base;
+  float* o_other = (float*)(base + lay.out_bytes);
+  float* row_cos = (float*)(base + 2 * lay.out_bytes);
+  void* tail = lay.tail_bytes ? (void*)(base + 2 * lay.out_bytes + lay.cos_bytes) : nullptr;
+  const int64_t rows = (int64_t)layers[0].ix.batch * layers[0].ix.n_q;
+  st = hip_status(dsa_host::identity_f64_launch(S, n, stream), "matrix fill launch");
+  if (st != DSA_OK) return st;
+  // every layer F: T_l = Top-k of its own indexer
+  for (int32_t l = 0; l < n; ++l) {
+    st = run_topk(&layers[l].ix, nullptr, k, layers[l].idx_out, tail, stream);
+    if (st != DSA_OK) return st;
+  }
+  for (int32_t i = 1; i < n; ++i) {
+    dsa_sparse_attn_args sa = layers[i].sa;
+    const int64_t width = (int64_t)sa.heads * sa.d_v;
+    sa.idx = layers[i].idx_out;
+    sa.out = o_own;
+    st = hip_status(dsa_host::sparse_attn_launch(sa, tail, stream), "sparse attention launch");
+    if (st != DSA_OK) return st;
+    for (int32_t j = 0; j < i; ++j) {
+      sa.idx = layers[j].idx_out;
+      sa.out = o_other;
+      st = hip_status(dsa_host::sparse_attn_launch(sa, tail, stream), "sparse attention launch");
+      if (st != DSA_OK) return st;
+      st = hip_status(dsa_host::row_cosine_launch(o_own, o_other, rows, width, row_cos, S + (int64_t)i * n + j,
+                                                  stream),
+                      "cosine launch");
+      if (st != DSA_OK) return st;
+    }
+  }
+  return DSA_OK;
+}
+
+dsa_status dsa_pattern_search(const double* S, int32_t n, int32_t n_full, char* pattern, double* score) {
+  g_last_error.clear();
+  if (n < 1 || n > 1024) return fail(DSA_ERR_INVALID, "n_layers must be 1..1024");
+  if (n_full < 1 || n_full > n) return fail(DSA_ERR_INVALID, "n_full must be 1..n_layers");
+  if (!S || !pattern) return fail(DSA_ERR_INVALID, "S and pattern are required");
+  for (int32_t i = 1; i < n; ++i)
+    for (int32_t j = 0; j < i; ++j)
+      if (!std::isfinite(S[(int64_t)i * n + j])) return fail(DSA_ERR_INVALID, "S[%d, %d] is not finite", i, j);
+  if (!dsa_host::pattern_search_dp(S, n, n_full, pattern, score))
+    return fail(DSA_ERR_INVALID, "no admissible pattern");
+  return DSA_OK;
 }
 
 }  // extern "C"

@@ -143,4 +143,12 @@ hipError_t sparse_attn_launch(const dsa_sparse_attn_args& a, void* ws, hipStream
 hipError_t overlap_launch(const int32_t* a, const int32_t* b, int64_t rows, int32_t k,
                           int32_t* row_counts, unsigned long long* total, hipStream_t s);
 
+// Output similarity for the pattern search (similarity.hip).
+hipError_t row_cosine_launch(const float* a, const float* b, int64_t rows, int64_t width, float* row_cos,
+                             double* mean, hipStream_t s);
+hipError_t identity_f64_launch(double* m, int64_t n, hipStream_t s);
+// Sharing-pattern dynamic program, host code (pattern_search.cpp).  False if no
+// admissible pattern exists.
+bool pattern_search_dp(const double* S, int n, int M, char* pattern, double* score);
+
 }  // namespace dsa_host

@@ -236,6 +236,67 @@ typedef struct dsa_distill_args {
 
 dsa_status dsa_indexer_distill(const dsa_distill_args* args, hipStream_t stream);
 
+/*
+ * Per-row cosine similarity of two outputs ([IC-SUMMARY] Appendix C: the
+ * similarity-based pattern search compares attention outputs by cosine
+ * similarity):
+ *     row_cos[r] = <a_r, b_r> / (|a_r| |b_r|)
+ * over the width values of row r (for an attention output [rows, heads, d_v]:
+ * every head and value column of one query row).  A row pair where both rows
+ * are zero gives 1, exactly one zero row gives 0.  The three sums are taken in
+ * float64 in a fixed order (the result repeats bit for bit).
+ *   a, b     device fp32 [rows, width], row-major and dense, 16-byte aligned
+ *   rows     1 .. 2^31 - 1;  width: a multiple of 4, 4 .. 2^26
+ *   row_cos  device fp32 [rows] out (required)
+ *   mean     device float64 [1] out, optional: the mean of row_cos over the
+ *            rows, summed in float64 in a fixed order
+ */
+dsa_status dsa_row_cosine(const float* a, const float* b, int64_t rows, int64_t width,
+                          float* row_cos, double* mean, hipStream_t stream);
+
+/*
+ * Similarity matrix of the pattern search ([IC-SUMMARY] Appendix C,
+ * construction of S).  Every layer runs INDEXER + Top-k (all layers F) into
+ * layers[l].idx_out; then for each layer i its attention output with its own
+ * index tensor, O_i, is compared with its output under every earlier layer j's
+ * index tensor:
+ *     S[i*N + j] = mean over the rows of row_cos(O_i, attention_i(T_j))  (i > j)
+ *     S[i*N + i] = 1,  S[i*N + j] = 0 for j > i            (N = n_layers)
+ *   layers[]  host array: ix and idx_out ([batch, n_q, k] int32) required for
+ *             every layer; sa as in indexcache_forward (sa.idx and sa.out are
+ *             ignored: the outputs go to the workspace).  Every layer has the
+ *             same batch and n_q; heads * d_v is a multiple of 4.
+ *   S         device float64 [N * N] out
+ *   ws        >= dsa_similarity_matrix_workspace_size bytes, 256-byte aligned
+ *             (the size depends on the shapes only; idx_out may be NULL when
+ *             sizing)
+ * Work on stream: N Top-k calls, N - 1 + N(N-1)/2 attention calls, N(N-1)/2 cosine
+ * calls.  n_layers 1..1024.
+ */
+size_t dsa_similarity_matrix_workspace_size(int32_t n_layers, const dsa_layer* layers, int32_t k);
+dsa_status dsa_similarity_matrix(int32_t n_layers, const dsa_layer* layers, int32_t k, double* S,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Sharing-pattern search by dynamic programming ([IC-SUMMARY] Appendix C):
+ * the pattern of n_layers layers, layer 0 F and exactly n_full F layers, that
+ * maximises the total similarity
+ *     sum over the S layers l of S[l, src(l)],  src(l) = the nearest F layer before l
+ * (F layers add nothing).  dp[i][m] is the best total of layers 0..i with m F
+ * layers and layer i F: dp[i][m] = max_{j<i} dp[j][m-1] + sum_{j<l<i} S[l, j];
+ * the answer is max_i dp[i][n_full] + sum_{l>i} S[l, i], and backtracking the
+ * choices gives the pattern.  Host code, no GPU work, O(n_layers^2 n_full).
+ *   S        host float64 [n_layers * n_layers]; only S[i*N + j] with i > j is
+ *            read, and must be finite
+ *   n_layers 1..1024;  n_full 1..n_layers
+ *   pattern  host char [n_layers + 1] out: 'F'/'S', NUL-terminated
+ *   score    host float64 out, optional: the pattern's total
+ * Ties: each dp step keeps the earliest predecessor, the last step the earliest
+ * final F layer.
+ */
+dsa_status dsa_pattern_search(const double* S, int32_t n_layers, int32_t n_full, char* pattern,
+                              double* score);
+
 #ifdef __cplusplus
 }
 #endif

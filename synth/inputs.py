@@ -28,7 +28,7 @@ __all__ = [
     "F32", "BF16", "FP8", "IndexerInputs", "SAInputs", "generator",
     "fp8_encode_vectors", "indexer_inputs", "sa_inputs", "random_sorted_indices",
     "c4_stack", "c5_layer_indexer", "c5_layer_sa", "CONFIGS", "C5_PATTERN",
-    "uniform_pattern", "SEARCHED_PATTERNS_47",
+    "uniform_pattern", "SEARCHED_PATTERNS_47", "drift_stack",
 ]
 
 
@@ -253,3 +253,41 @@ def c5_layer_indexer(layer: int, *, B=8, S=204800, H=64, d=128, seed=5, device="
 def c5_layer_sa(layer: int, *, B=8, S=204800, heads=16, d_qk=576, d_v=512, seed=5, device="cpu"):
     return sa_inputs(B=B, n_q=1, n_k=S, heads=heads, kv_heads=1, d_qk=d_qk, d_v=d_v,
                      latent=True, dtype=BF16, seed=seed * 1000 + 300 + layer, device=device)
+
+
+def drift_stack(*, n_layers, B=1, n_q, n_k=None, q_pos0=0, H=64, d=128, dtype=BF16, values="normal",
+                rho=0.9, rho_jump=0.2, p_jump=0.15, seed=6, device="cpu", sa_heads=16, d_qk=576, d_v=512):
+    """Calibration stack for the similarity-based pattern search.  The indexer
+    queries and head weights are drawn once and shared by every layer; the
+    indexer keys drift with depth, so nearby layers select overlapping index
+    sets and distant ones less:
+      normal: k_0 ~ N(0, 1);   k_l = rho_l k_{l-1} + sqrt(1 - rho_l^2) e_l,  e_l ~ N(0, 1)
+      int:    k_0 ~ U{-3..3};  k_l = k_{l-1} with each entry redrawn with probability 1 - rho_l
+    rho_l = rho_jump on "jump" layers (each layer >= 1 is one with probability
+    p_jump), else rho.  Keys are stored as ``dtype`` (fp8 with per-token
+    scales).  Every layer has its own sparse-attention inputs (MLA latent rows).
+    Returns (layers [(IndexerInputs, SAInputs)], jumps [bool])."""
+    if n_k is None:
+        n_k = q_pos0 + n_q
+    g = generator(seed, device)
+    shared = indexer_inputs(B=B, n_q=n_q, n_k=1, H=H, d=d, q_pos0=q_pos0, dtype=dtype, values=values,
+                            w_dist="u8" if values == "normal" else "pow2", seed=seed * 1000 + 1, device=device)
+    jumps = (torch.rand(n_layers, generator=g, device=device) < p_jump).cpu().tolist()
+    jumps[0] = False
+    kf = _draw(g, (B, n_k, d), device, values)
+    layers = []
+    for l in range(n_layers):
+        if l > 0:
+            r = rho_jump if jumps[l] else rho
+            if values == "int":
+                redraw = torch.rand((B, n_k, d), generator=g, device=device) < (1.0 - r)
+                kf = torch.where(redraw, _draw(g, (B, n_k, d), device, "int"), kf)
+            else:
+                kf = r * kf + (1.0 - r * r) ** 0.5 * _draw(g, (B, n_k, d), device, values)
+        k, ks = _store(kf, dtype, values)
+        ix = IndexerInputs(dtype=dtype, q=shared.q, k=k, w=shared.w, q_scale=shared.q_scale, k_scale=ks,
+                           q_pos0=q_pos0)
+        sa = sa_inputs(B=B, n_q=n_q, n_k=n_k, heads=sa_heads, kv_heads=1, d_qk=d_qk, d_v=d_v, latent=True,
+                       dtype=BF16, seed=seed * 1000 + 100 + l, device=device)
+        layers.append((ix, sa))
+    return layers, jumps

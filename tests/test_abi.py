@@ -193,3 +193,40 @@ def test_distill_rejects(kw, expect):
 
 def test_distill_null_args():
     assert L.dsa_indexer_distill(None, None) == 1
+
+
+def test_row_cosine_rejects():
+    ok = dict(a=FAKE, b=FAKE, rows=4, width=8192, row_cos=FAKE, mean=None)
+
+    def st(**kw):
+        a = dict(ok, **kw)
+        return L.dsa_row_cosine(a["a"], a["b"], a["rows"], a["width"], a["row_cos"], a["mean"], None)
+    for kw in (dict(rows=0), dict(rows=1 << 31), dict(width=6), dict(width=0), dict(width=(1 << 26) + 4),
+               dict(a=None), dict(b=None), dict(row_cos=None), dict(a=FAKE + 8), dict(mean=FAKE + 4)):
+        assert st(**kw) == 1, kw
+        assert L.dsa_last_error() != b""
+
+
+def test_similarity_matrix_validation_and_workspace():
+    arr = layers("FFF", null_s=False)
+    need = L.dsa_similarity_matrix_workspace_size(3, arr, 16)
+    # two outputs of 4 rows x 16 heads x 512 fp32 and the row cosines at least
+    assert need >= 2 * 4 * 16 * 512 * 4
+    assert L.dsa_similarity_matrix(3, arr, 16, FAKE, None, 0, None) == 3       # workspace missing
+    assert L.dsa_similarity_matrix(3, arr, 16, FAKE, FAKE, need - 1, None) == 3
+    assert L.dsa_similarity_matrix(3, arr, 16, None, FAKE, need, None) == 1    # S missing
+    assert L.dsa_similarity_matrix(0, arr, 16, FAKE, FAKE, need, None) == 1
+    assert L.dsa_similarity_matrix(3, arr, 0, FAKE, FAKE, need, None) == 1
+    bad = layers("FFF", null_s=False)
+    bad[2].idx_out = None                                   # every layer needs its T (not to size the workspace)
+    assert L.dsa_similarity_matrix_workspace_size(3, bad, 16) == need
+    assert L.dsa_similarity_matrix(3, bad, 16, FAKE, FAKE, need, None) == 1
+    bad = layers("FFF", null_s=False)
+    bad[1].sa.n_q = 5                                                          # rows must agree
+    assert L.dsa_similarity_matrix(3, bad, 16, FAKE, FAKE, need, None) == 1
+    assert L.dsa_similarity_matrix(3, None, 16, FAKE, FAKE, need, None) == 1
+    free = layers("FFF", null_s=False)
+    for a in free:
+        a.sa.out = None                                     # attention outputs live in the workspace
+        a.sa.idx = None
+    assert L.dsa_similarity_matrix_workspace_size(3, free, 16) == need
