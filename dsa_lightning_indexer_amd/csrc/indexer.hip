@@ -441,6 +441,12 @@ struct TileDma {
 __device__ __forceinline__ void lds_sync() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup"); }
 
 constexpr int kCandCap = 16384;        // candidates per row before a compaction
+// Rows shorter than kShortRow keys compact first at kShortFirstCap entries: their
+// final select then runs over a few thousand entries instead of up to 16384.
+// Longer rows keep the full first buffer (an early threshold is too loose there
+// and costs extra compactions later).
+constexpr int kShortRow = 32768;
+constexpr int kShortFirstCap = 8192;
 
 // Entries [j, j+4) of a candidate array in one 16-byte load.  The arrays are
 // 16-byte aligned and their capacity is a multiple of 4, so a load that starts
@@ -780,6 +786,7 @@ __global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk_kernel
     const int nkeys = (int)(t_last + 1 < p.n_k ? t_last + 1 : p.n_k);
     const int ntiles = (nkeys + TK - 1) / TK;
     const int tlim = t < p.n_k - 1 ? t : p.n_k - 1;             // last candidate position
+    const int first_cap = tlim < kShortRow ? kShortFirstCap : kCandCap;
     const int64_t gi = (int64_t)b * p.n_q + i;
 
     RowState<DT, D, HT> rs;
@@ -817,7 +824,7 @@ __global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk_kernel
           float v = sc[g];
           if constexpr (DT == DT_FP8) v *= *(const float*)(kt + C::TILE_BYTES + (64 * g + lane) * 4);
           const uint32_t u = order_key(v);
-          if (cnt + 64 > kCandCap) {
+          if (cnt + 64 > (full ? kCandCap : first_cap)) {
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
             const Shrunk sh = wave_shrink(cu, ci, cnt, k, hist[wid], lane);
             cnt = sh.n;
