@@ -67,7 +67,7 @@ def parse():
 
 
 def prefill_stack(dsa, syn, L, pattern, topk, dev):
-    layers = syn.c4_stack(L=L, n_layers=len(pattern), seed=4, device=dev)
+    layers = syn.prefill_stack_layers(L=L, n_layers=len(pattern), seed=4, device=dev)
     specs = []
     for l, (ix, sa) in enumerate(layers):
         spec = {"sa": {"q": sa.q, "kv": sa.kv, "scale": sa.scale, "d_v": 512,
@@ -83,11 +83,11 @@ def decode_stack(dsa, syn, B, S, n_layers, topk, dev):
     pattern = syn.uniform_pattern(n_layers, 4)
     specs = []
     for l, c in enumerate(pattern):
-        sa = syn.c5_layer_sa(l, B=B, S=S, device=dev)
+        sa = syn.decode_layer_sa(l, B=B, S=S, device=dev)
         spec = {"sa": {"q": sa.q, "kv": sa.kv, "scale": sa.scale, "d_v": 512,
                        "out": torch.empty((B, 1, 16, 512), dtype=torch.float32, device=dev)}}
         if c == "F":
-            ix = syn.c5_layer_indexer(l, B=B, S=S, device=dev)
+            ix = syn.decode_layer_indexer(l, B=B, S=S, device=dev)
             spec["ix"] = {"q": ix.q, "k": ix.k, "w": ix.w, "q_scale": ix.q_scale, "k_scale": ix.k_scale,
                           "q_pos0": ix.q_pos0}
             spec["idx_out"] = torch.empty((B, 1, topk), dtype=torch.int32, device=dev)
@@ -200,7 +200,7 @@ def profile_run(args, dev):
     L = args.prefill_len
     if args.profile == "attn":
         # the step's first prefill layer: its sparse attention over its F layer's index tensor
-        ix, sa = syn.c4_stack(L=L, n_layers=1, seed=4, device=dev)[0]
+        ix, sa = syn.prefill_stack_layers(L=L, n_layers=1, seed=4, device=dev)[0]
         idx = dsa.topk(ix.q, ix.k, ix.w, 2048)
         out = torch.empty((1, L, 16, 512), dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
@@ -209,7 +209,7 @@ def profile_run(args, dev):
             torch.cuda.synchronize()
             print(f"profile attn: prefill sparse attention L={L} launch {i + 1}/3 done", flush=True)
         return
-    ix = syn.c4_stack(L=L, n_layers=1, seed=4, device=dev, with_sa=False)[0][0]   # the step's first F layer
+    ix = syn.prefill_stack_layers(L=L, n_layers=1, seed=4, device=dev, with_sa=False)[0][0]   # the step's first F layer
     out = torch.empty((1, L, 2048), dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
     for i in range(3):
@@ -395,8 +395,8 @@ def sweep_run(args, dev):
 
     # decode stack: every layer has attention inputs; indexer inputs for any layer a pattern makes F
     B, S, NL = args.decode_batch, args.decode_len, args.decode_layers
-    sa = [syn.c5_layer_sa(l, B=B, S=S, device=dev) for l in range(NL)]
-    ix = [syn.c5_layer_indexer(l, B=B, S=S, device=dev) for l in range(NL)]
+    sa = [syn.decode_layer_sa(l, B=B, S=S, device=dev) for l in range(NL)]
+    ix = [syn.decode_layer_indexer(l, B=B, S=S, device=dev) for l in range(NL)]
     outs = [torch.empty((B, 1, 16, 512), dtype=torch.float32, device=dev) for _ in range(NL)]
     idxs = [torch.empty((B, 1, topk), dtype=torch.int32, device=dev) for _ in range(NL)]
     torch.cuda.synchronize()
@@ -434,7 +434,7 @@ def sweep_run(args, dev):
 
     # prefill stack
     L = args.prefill_len
-    layers = syn.c4_stack(L=L, n_layers=8, seed=4, device=dev)
+    layers = syn.prefill_stack_layers(L=L, n_layers=8, seed=4, device=dev)
     pouts = [torch.empty((1, L, 16, 512), dtype=torch.float32, device=dev) for _ in range(8)]
     pidx = [torch.empty((1, L, topk), dtype=torch.int32, device=dev) for _ in range(8)]
     torch.cuda.synchronize()
@@ -467,7 +467,7 @@ def sweep_run(args, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")

@@ -27,7 +27,7 @@ FP8_MAX = 448.0
 __all__ = [
     "F32", "BF16", "FP8", "IndexerInputs", "SAInputs", "generator",
     "fp8_encode_vectors", "indexer_inputs", "sa_inputs", "random_sorted_indices",
-    "c4_stack", "c5_layer_indexer", "c5_layer_sa", "CONFIGS", "C5_PATTERN",
+    "prefill_stack_layers", "decode_layer_indexer", "decode_layer_sa", "WORKLOADS", "DECODE_PATTERN",
     "uniform_pattern", "SEARCHED_PATTERNS_47", "drift_stack",
 ]
 
@@ -182,7 +182,7 @@ def uniform_pattern(n_layers: int, r: int) -> str:
     return "".join("F" if i % r == 0 else "S" for i in range(n_layers))
 
 
-C5_PATTERN = uniform_pattern(47, 4)   # F at layers 1,5,...,45 (1-based): 12 F layers
+DECODE_PATTERN = uniform_pattern(47, 4)   # F at layers 1,5,...,45 (1-based): 12 F layers
 
 # Greedy-searched sharing patterns of the 47-layer GLM-4.7-Flash 30B DSA model at
 # retention 1/2, 1/4 and 1/8 ([DSA-NOTES] Appendix B, "搜索到的模式"): data for the
@@ -197,25 +197,25 @@ SEARCHED_PATTERNS_47 = {
 
 
 # --- named workloads ---------------------------------------------------------
-CONFIGS = {
-    1: dict(name="tiny fp32 F layer L=512 H_I=4 d_I=32 k=64", L=512, H=4, d=32, dtype=F32,
+WORKLOADS = {
+    "tiny_fp32_L512": dict(name="tiny fp32 F layer L=512 H_I=4 d_I=32 k=64", L=512, H=4, d=32, dtype=F32,
             values="int", w_dist="pow2", topk=64, sa_heads=4, sa_kv_heads=4, sa_d=64, seed=1),
-    2: dict(name="bf16 prefill indexer L=16384 H_I=64 d_I=128 k=2048", L=16384, H=64, d=128,
+    "prefill_bf16_L16384": dict(name="bf16 prefill indexer L=16384 H_I=64 d_I=128 k=2048", L=16384, H=64, d=128,
             dtype=BF16, values="normal", w_dist="u8", topk=2048, seed=2),
-    3: dict(name="fp8 prefill indexer+SA L=65536 H_I=64 d_I=128 k=2048, SA 16 heads 576/512",
+    "prefill_fp8_L65536": dict(name="fp8 prefill indexer+SA L=65536 H_I=64 d_I=128 k=2048, SA 16 heads 576/512",
             L=65536, H=64, d=128, dtype=FP8, values="normal", w_dist="u8", topk=2048,
             sa_heads=16, sa_d_qk=576, sa_d_v=512, seed=3),
-    4: dict(name="8-layer IndexCache prefill stack L=131072 FSSSFSSS vs FFFFFFFF", L=131072,
+    "stack_bf16_L131072": dict(name="8-layer IndexCache prefill stack L=131072 FSSSFSSS vs FFFFFFFF", L=131072,
             H=64, d=128, dtype=BF16, topk=2048, layers=8, sa_heads=16, sa_d_qk=576,
             sa_d_v=512, seed=4),
-    5: dict(name="47-layer decode stack B=8 S=204800 FSSS k=2048", B=8, S=204800, layers=47,
+    "decode_fp8_B8_S204800": dict(name="47-layer decode stack B=8 S=204800 FSSS k=2048", B=8, S=204800, layers=47,
             H=64, d=128, dtype=FP8, topk=2048, sa_heads=16, sa_d_qk=576, sa_d_v=512, seed=5),
 }
 
 
-def c4_stack(*, L, n_layers=8, H=64, d=128, noise=0.3, seed=4, device="cpu", values="normal",
+def prefill_stack_layers(*, L, n_layers=8, H=64, d=128, noise=0.3, seed=4, device="cpu", values="normal",
              with_sa=True, sa_heads=16, d_qk=576, d_v=512):
-    """Config-4 style stack: q and w drawn once and shared by every layer; layer l's
+    """8-layer prefill stack (L = 131072 in the benchmark): q and w drawn once and shared by every layer; layer l's
     indexer keys are bf16(base_k + noise * N(0,1)_l) with base_k ~ N(0,1) in bf16;
     every layer has independent sparse-attention Q/KV."""
     g = generator(seed, device)
@@ -241,7 +241,7 @@ def c4_stack(*, L, n_layers=8, H=64, d=128, noise=0.3, seed=4, device="cpu", val
     return layers
 
 
-def c5_layer_indexer(layer: int, *, B=8, S=204800, H=64, d=128, seed=5, device="cpu",
+def decode_layer_indexer(layer: int, *, B=8, S=204800, H=64, d=128, seed=5, device="cpu",
                      values="normal"):
     """Decode F layer: one new query per sequence at position S-1 against an fp8
     e4m3fn indexer K cache [B, S, d] with per-token scales; w ~ N(0,1) (signed)."""
@@ -250,7 +250,7 @@ def c5_layer_indexer(layer: int, *, B=8, S=204800, H=64, d=128, seed=5, device="
                           seed=seed * 1000 + 200 + layer, device=device)
 
 
-def c5_layer_sa(layer: int, *, B=8, S=204800, heads=16, d_qk=576, d_v=512, seed=5, device="cpu"):
+def decode_layer_sa(layer: int, *, B=8, S=204800, heads=16, d_qk=576, d_v=512, seed=5, device="cpu"):
     return sa_inputs(B=B, n_q=1, n_k=S, heads=heads, kv_heads=1, d_qk=d_qk, d_v=d_v,
                      latent=True, dtype=BF16, seed=seed * 1000 + 300 + layer, device=device)
 

@@ -37,8 +37,8 @@ def check_sa(dsa, sa, idx, rows=None):
     return got
 
 
-def test_c1_fp32_mha(dsa, dev):
-    c = syn.CONFIGS[1]
+def test_tiny_fp32_mha(dsa, dev):
+    c = syn.WORKLOADS["tiny_fp32_L512"]
     L = c["L"]
     sa = syn.sa_inputs(n_q=L, n_k=L, heads=4, kv_heads=4, d_qk=64, d_v=64, latent=False, dtype=syn.F32,
                        seed=c["seed"], device=dev)

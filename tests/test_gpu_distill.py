@@ -82,7 +82,7 @@ def test_distill_signed_weights_and_worked_example_shape(dsa, dev):
 
 
 def test_distill_full_size_sampled_and_homogeneity(dsa, dev):
-    """One F layer at the C2 shape (L = 16384, H = 64, d = 128, k = 2048) with
+    """One F layer at the bf16 prefill shape (L = 16384, H = 64, d = 128, k = 2048) with
     four teachers: sampled rows against the oracle; dk through identities that
     hold at any size (z is degree-1 homogeneous in q, w and k):
         sum_j w_j dw_j = sum_j q_j . dq_j = sum_e delta_e z_e   per row,

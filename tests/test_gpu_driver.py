@@ -21,7 +21,7 @@ def dsa():
 
 
 def build_stack(dev, pattern, L, topk, values="int"):
-    layers = syn.c4_stack(L=L, n_layers=len(pattern), seed=40, device=dev, values=values)
+    layers = syn.prefill_stack_layers(L=L, n_layers=len(pattern), seed=40, device=dev, values=values)
     specs = []
     for l, (ix, sa) in enumerate(layers):
         out = torch.zeros((1, L, 16, 512), dtype=torch.float32, device=dev)
@@ -95,11 +95,11 @@ def test_decode_stack_fsss(dsa, dev):
     pattern, B, S, topk = "FSSSFSSSF", 2, 5000, 2048
     specs, ixs, sas = [], [], []
     for l, c in enumerate(pattern):
-        sa = syn.c5_layer_sa(l, B=B, S=S, device=dev)
+        sa = syn.decode_layer_sa(l, B=B, S=S, device=dev)
         sas.append(sa)
         out = torch.zeros((B, 1, 16, 512), device=dev)
         spec = {"sa": {"q": sa.q, "kv": sa.kv, "scale": sa.scale, "out": out, "d_v": 512}}
-        ix = syn.c5_layer_indexer(l, B=B, S=S, device=dev, values="int") if c == "F" else None
+        ix = syn.decode_layer_indexer(l, B=B, S=S, device=dev, values="int") if c == "F" else None
         ixs.append(ix)
         if ix is not None:
             spec["ix"] = {"q": ix.q, "k": ix.k, "w": ix.w, "q_scale": ix.q_scale, "k_scale": ix.k_scale,
@@ -163,10 +163,10 @@ def test_decode_stack_graph_replay(dsa, dev):
     pattern, B, S, topk = "FSSSFSSSF", 2, 6000, 2048
     specs, ixs = [], []
     for l, c in enumerate(pattern):
-        sa = syn.c5_layer_sa(l, B=B, S=S, device=dev)
+        sa = syn.decode_layer_sa(l, B=B, S=S, device=dev)
         out = torch.zeros((B, 1, 16, 512), device=dev)
         spec = {"sa": {"q": sa.q, "kv": sa.kv, "scale": sa.scale, "out": out, "d_v": 512}}
-        ix = syn.c5_layer_indexer(l, B=B, S=S, device=dev, values="int") if c == "F" else None
+        ix = syn.decode_layer_indexer(l, B=B, S=S, device=dev, values="int") if c == "F" else None
         ixs.append(ix)
         if ix is not None:
             spec["ix"] = {"q": ix.q, "k": ix.k, "w": ix.w, "q_scale": ix.q_scale, "k_scale": ix.k_scale,

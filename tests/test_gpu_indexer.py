@@ -66,9 +66,9 @@ def check_float(dsa, ixi, topk, rows):
     return got
 
 
-# --------------------------------------------------------------------------- config 1
-def test_c1_tiny_fp32_exact(dsa, dev):
-    c = syn.CONFIGS[1]
+# --------------------------------------------------------------------------- tiny fp32 layer (L=512)
+def test_tiny_fp32_exact(dsa, dev):
+    c = syn.WORKLOADS["tiny_fp32_L512"]
     ixi = syn.indexer_inputs(n_q=c["L"], H=c["H"], d=c["d"], dtype=syn.F32, values="int",
                              w_dist="pow2", seed=c["seed"], device=dev)
     check_exact(dsa, ixi, c["topk"])
@@ -206,15 +206,15 @@ def test_decode_scan_integer_exact_and_matches_prefill_row(dsa, dev, dtype):
 
 
 def test_decode_scan_float_signed_w(dsa, dev):
-    ixi = syn.c5_layer_indexer(0, B=4, S=7000, device=dev)
+    ixi = syn.decode_layer_indexer(0, B=4, S=7000, device=dev)
     check_float(dsa, ixi, 2048, np.array([0]))
 
 
-def test_decode_full_size_c5_layer(dsa, dev):
+def test_decode_full_size_layer(dsa, dev):
     """One decode F layer at full size: B=8 sequences, 204800 cached fp8 keys."""
-    ixi = syn.c5_layer_indexer(0, device=dev)
+    ixi = syn.decode_layer_indexer(0, device=dev)
     check_float(dsa, ixi, 2048, np.array([0]))
-    ixi = syn.c5_layer_indexer(1, device=dev, values="int")
+    ixi = syn.decode_layer_indexer(1, device=dev, values="int")
     check_exact(dsa, ixi, 2048)
 
 
@@ -243,19 +243,19 @@ def test_fused_prefill_compaction_float(dsa, dev):
     check_float(dsa, ixi, 2048, np.array([16383, 16384, 25000, L - 1]))
 
 
-@pytest.mark.parametrize("cid", [2, 3])
-def test_full_size_configs_sampled(dsa, dev, cid):
-    """Configs 2 (bf16, L=16384) and 3 (fp8, L=65536) at full size, in the launch
+@pytest.mark.parametrize("wl", ["prefill_bf16_L16384", "prefill_fp8_L65536"])
+def test_full_size_prefill_sampled(dsa, dev, wl):
+    """The bf16 L=16384 and fp8 L=65536 prefill layers at full size, in the launch
     configuration the benchmark uses; sampled rows against the oracle."""
-    c = syn.CONFIGS[cid]
+    c = syn.WORKLOADS[wl]
     ixi = syn.indexer_inputs(B=1, n_q=c["L"], dtype=c["dtype"], values="normal", w_dist="u8", seed=c["seed"],
                              device=dev)
     rows = np.array([0, 2046, 2047, 2048, c["L"] // 2, c["L"] - 1])
     check_float(dsa, ixi, c["topk"], rows)
 
 
-def test_full_size_config4_layer_integer_exact(dsa, dev):
+def test_full_size_stack_layer_integer_exact(dsa, dev):
     """One F layer of the 8-layer L=131072 stack, integer-valued variant."""
-    layers = syn.c4_stack(L=131072, n_layers=1, seed=4, device=dev, values="int", with_sa=False)
+    layers = syn.prefill_stack_layers(L=131072, n_layers=1, seed=4, device=dev, values="int", with_sa=False)
     ixi = layers[0][0]
     check_exact(dsa, ixi, 2048, rows=np.array([5, 4095, 65536, 131070, 131071]))

@@ -313,9 +313,9 @@ def test_pattern_rules():
         oracle.source_layers("FXF")
     assert oracle.source_layers("F") == [1]
     assert oracle.source_layers("FFSF") == [1, 2, 2, 4]
-    assert oracle.source_layers(syn.C5_PATTERN).count(None) == 0
-    assert syn.C5_PATTERN.count("F") == 12 and len(syn.C5_PATTERN) == 47
-    assert [i + 1 for i, c in enumerate(syn.C5_PATTERN) if c == "F"] == list(range(1, 46, 4))
+    assert oracle.source_layers(syn.DECODE_PATTERN).count(None) == 0
+    assert syn.DECODE_PATTERN.count("F") == 12 and len(syn.DECODE_PATTERN) == 47
+    assert [i + 1 for i, c in enumerate(syn.DECODE_PATTERN) if c == "F"] == list(range(1, 46, 4))
 
 
 def test_searched_patterns_from_the_page():
