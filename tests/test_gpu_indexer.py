@@ -228,19 +228,22 @@ def test_determinism(dsa, dev):
 # --------------------------------------------------------------------------- long rows
 @pytest.mark.parametrize("dtype", [syn.BF16, syn.FP8])
 def test_fused_prefill_compaction_integer_exact(dsa, dev, dtype):
-    """Rows longer than the 16384-entry candidate buffer force compactions.  With
-    integer scores ties are massive, so the 16-bit-prefix shrink cannot free
-    space and the exact select (ties to the lower position) takes over."""
+    """Rows longer than the candidate buffer force compactions (rows shorter than
+    32768 keys compact first at 8192 candidates, longer ones at 16384: rows on
+    both sides of both limits).  With integer scores ties are massive, so the
+    16-bit-prefix shrink cannot free space and the exact select (ties to the
+    lower position) takes over."""
     L = 40000
     ixi = syn.indexer_inputs(B=1, n_q=L, dtype=dtype, values="int", w_dist="pow2", seed=31, device=dev)
-    rows = np.array([0, 2047, 16383, 16384, 16400, 20000, 33333, L - 2, L - 1])
+    rows = np.array([0, 2047, 8191, 8192, 8300, 16383, 16384, 16400, 20000, 32766, 32767, 32768, 33333,
+                     L - 2, L - 1])
     check_exact(dsa, ixi, 2048, rows=rows)
 
 
 def test_fused_prefill_compaction_float(dsa, dev):
     L = 40000
     ixi = syn.indexer_inputs(B=1, n_q=L, dtype=syn.BF16, values="normal", w_dist="u8", seed=32, device=dev)
-    check_float(dsa, ixi, 2048, np.array([16383, 16384, 25000, L - 1]))
+    check_float(dsa, ixi, 2048, np.array([8191, 8192, 16383, 16384, 25000, 32767, 32768, L - 1]))
 
 
 @pytest.mark.parametrize("wl", ["prefill_bf16_L16384", "prefill_fp8_L65536"])
