@@ -58,6 +58,10 @@ def parse():
                         "the dynamic-program patterns at 24/12/7 F layers; prints one JSON object")
     p.add_argument("--similarity-len", type=int, default=16384)
     p.add_argument("--similarity-layers", type=int, default=47)
+    p.add_argument("--layer", choices=["prefill_bf16_L16384", "prefill_fp8_L65536"], default=None,
+                   help="one prefill F layer of a named workload instead of the bench line: the fused "
+                        "indexer+Top-k (and, for the fp8 layer, its 16-head MLA sparse attention) timed with HIP "
+                        "events over --kernel-reps launches; prints one JSON object")
     p.add_argument("--profile", choices=["indexer", "attn", "copy"], default=None,
                    help="counter-collection runs: 'indexer' launches only the prefill F layer's fused "
                         "indexer+Top-k (3 launches, the first a warm-up); 'attn' that layer's prefill "
@@ -216,6 +220,48 @@ def profile_run(args, dev):
         dsa.topk(ix.q, ix.k, ix.w, 2048, out=out)
         torch.cuda.synchronize()
         print(f"profile indexer: fused indexer+Top-k L={L} launch {i + 1}/3 done", flush=True)
+
+
+def layer_run(args, dev):
+    """One prefill F layer of a named workload: fused indexer+Top-k, plus (fp8
+    layer) the sparse attention over its index tensor."""
+    import dsa_lightning_indexer_amd as dsa
+    from synth import inputs as syn
+    c = syn.WORKLOADS[args.layer]
+    L, topk = c["L"], c["topk"]
+    ix = syn.indexer_inputs(B=1, n_q=L, H=c["H"], d=c["d"], dtype=c["dtype"], values=c["values"],
+                            w_dist=c["w_dist"], seed=c["seed"], device=dev)
+    out = torch.empty((1, L, topk), dtype=torch.int32, device=dev)
+    run = lambda: dsa.topk(ix.q, ix.k, ix.w, topk, q_scale=ix.q_scale, k_scale=ix.k_scale, out=out)
+    run()
+    torch.cuda.synchronize()
+    ts = time_launches(run, max(args.kernel_reps, 3))
+    ms = sum(ts) / len(ts)
+    flop = L * (L + 1) / 2 * 2 * c["H"] * c["d"]
+    fp8 = c["dtype"] == syn.FP8
+    peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+    rec = {"metric": "indexer+Top-k score-pairs/s", "value": L * (L + 1) / 2 / (ms * 1e-3), "unit": "score-pairs/s",
+           "n_gpus": 1, "higher_is_better": True, "ms_per_launch": ms, "launches": len(ts),
+           "dtype": c["dtype"], "data": "synthetic", "config": {"workload": c["name"]},
+           "roofline": {"bound": "mfma", "achieved": flop / (ms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s",
+                        "frac": flop / (ms * 1e-3) / 1e12 / peak,
+                        "algorithmic_per_launch": f"{L * (L + 1) // 2} causal pairs x {2 * c['H'] * c['d']} flop"}}
+    log(f"{args.layer}: fused indexer+Top-k {ms:.3f} ms/launch")
+    if fp8:
+        sa = syn.sa_inputs(B=1, n_q=L, n_k=L, heads=c["sa_heads"], d_qk=c["sa_d_qk"], d_v=c["sa_d_v"], seed=c["seed"],
+                           device=dev)
+        o = torch.empty((1, L, c["sa_heads"], c["sa_d_v"]), dtype=torch.float32, device=dev)
+        sa_run = lambda: dsa.sparse_attn(sa.q, sa.kv, out, sa.scale, d_v=sa.d_v, out=o)
+        sa_run()
+        torch.cuda.synchronize()
+        t_sa = time_launches(sa_run, max(args.kernel_reps, 3))
+        sa_ms = sum(t_sa) / len(t_sa)
+        gathered = int((out >= 0).sum().item()) * c["sa_d_qk"] * 2
+        rec["sparse_attn"] = {"ms_per_launch": sa_ms, "gathered_bytes": gathered,
+                              "gathered_TBps": gathered / (sa_ms * 1e-3) / 1e12,
+                              "tokens_per_s": L / (sa_ms * 1e-3)}
+        log(f"{args.layer}: sparse attention {sa_ms:.3f} ms/launch")
+    print(json.dumps(rec), flush=True)
 
 
 def distill_run(args, dev):
@@ -483,6 +529,9 @@ def main():
         return
     if args.similarity:
         similarity_run(args, dev)
+        return
+    if args.layer:
+        layer_run(args, dev)
         return
     import dsa_lightning_indexer_amd as dsa
     from synth import inputs as syn
