@@ -120,10 +120,10 @@ hipError_t indexer_scores_f32(const dsa_indexer_args& a, int64_t row0, int64_t r
                               int64_t out_row_stride, hipStream_t s);
 hipError_t indexer_scores_mfma(const dsa_indexer_args& a, int64_t row0, int64_t rows, float* out,
                                hipStream_t s);
-// Fused prefill INDEXER + Top-k: persistent grid with one query row per wave;
-// each of at most kTopkWaveSlots waves owns a candidate slice in the workspace
-// (topk_fused_ws_bytes()).
-constexpr int kTopkWaveSlots = 2048;
+// Fused prefill INDEXER + Top-k: persistent grid, one or two query rows per
+// wave; each query row in flight owns one of kTopkWaveSlots candidate slices in
+// the workspace (topk_fused_ws_bytes()).
+constexpr int kTopkWaveSlots = 4096;
 size_t topk_fused_ws_bytes();
 hipError_t indexer_topk_fused(const dsa_indexer_args& a, int32_t k, int32_t* idx, void* ws, hipStream_t s);
 // Decode-shaped scan: fp32 scores of every (row, s) into `scores` [batch*n_q, n_k],

@@ -862,6 +862,278 @@ __global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk_kernel
   }
 }
 
+// ---------------------------------------------------------------- fused, two rows per wave (bf16, d = 128)
+// v_mfma_f32_16x16x32_bf16 tiles: A = 16 heads of one query row, B = 16 keys
+// (K^T), both with lane (g = lane >> 4, c = lane & 15) holding row/column c and
+// K elements 8g..8g+7 of the 32-wide step; D lane (g, c) holds key c, heads
+// 4g..4g+3 of the tile.  A wave owns two adjacent query rows, so every key
+// fragment read from LDS feeds both rows' MFMAs and a workgroup's staged tiles
+// serve eight rows.
+__device__ __forceinline__ float quad_sum2(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+struct Row2 {
+  bf16x8 a[2][4][4];   // [row][head tile][K step]
+};
+
+// q fragments of row j into registers; its head weights into the wave's LDS
+// table w2[j][0..64) (zero for heads >= H), read back by the epilogue with
+// broadcast loads (the lanes of one 16-lane group read the same 4 weights).
+__device__ __forceinline__ void load_row2(const IxParams& p, int64_t gi, bool valid, int j, int lane, Row2& rs,
+                                          float (*w2)[64]) {
+  const int g = lane >> 4, col = lane & 15;
+  const __bf16* qb = (const __bf16*)p.q;
+  w2[j][lane] = (valid && lane < p.heads) ? p.w[gi * p.heads + lane] : 0.f;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const int head = 16 * h + col;
+    if (valid && head < p.heads) {
+      const __bf16* rowp = qb + (gi * p.heads + head) * 128 + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) rs.a[j][h][ks] = *(const bf16x8*)(rowp + 32 * ks);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) rs.a[j][h][ks] = bf16x8{};
+    }
+  }
+}
+
+__device__ __forceinline__ void settle_row2(Row2& rs) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(rs.a[j][h][ks]));
+    }
+}
+
+// Scores of the 64 keys of an LDS tile for both rows: lane l gets key l.  The
+// rows are staggered by half a 16-key step so that each row's ReLU-w epilogue
+// runs under the other row's MFMAs: row 0 of step t+1 is multiplied while row 1
+// of step t is summed, with one row's accumulators in flight at a time.
+__device__ __forceinline__ void mfma_row2(const bf16x8 (&a)[4][4], const bf16x8 (&bf)[4], f32x4 (&acc)[4]) {
+#pragma unroll
+  for (int h = 0; h < 4; ++h) acc[h] = f32x4{};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[h][ks], bf[ks], acc[h], 0, 0, 0);
+}
+// This lane's part of the head sum (its 16 heads) for key col of one step.
+__device__ __forceinline__ float epi_row2(const f32x4 (&acc)[4], const float* w, int g) {
+  float pp = 0.f;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const f32x4 cw = *(const f32x4*)&w[16 * h + 4 * g];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pp = fmaf(cw[i], fmaxf(acc[h][i], 0.f), pp);
+  }
+  return pp;
+}
+// Reduce-scatter of the four steps' parts over the four 16-lane groups: lane
+// (g, c) ends with the full sum of step g, key 16 g + c, i.e. key `lane`.
+// v_permlane16_swap(x, y) swaps x's odd 16-lane rows with y's even rows, so
+// x + y then holds x's step in the even rows and y's in the odd rows, each
+// summed over the row pair; v_permlane32_swap does the same across halves.
+__device__ __forceinline__ float scatter4(float p0, float p1, float p2, float p3) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+  const float sa = __uint_as_float(a[0]) + __uint_as_float(a[1]);       // row r: step r & 1, rows {r, r ^ 1}
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(p2), __float_as_uint(p3), false, false);
+  const float sb = __uint_as_float(b[0]) + __uint_as_float(b[1]);       // row r: step 2 + (r & 1)
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(sa), __float_as_uint(sb), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);                 // row r: step r, all four rows
+}
+__device__ __forceinline__ void load_bf2(const uint8_t* kt, int t, int g, int col, bf16x8 (&bf)[4]) {
+  typedef Cfg<DT_BF16, 128> C;
+  const uint8_t* rowp = kt + (16 * t + col) * C::PITCH + 16 * g;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) bf[ks] = *(const bf16x8*)(rowp + 64 * ks);
+}
+__device__ __forceinline__ void tile_scores2(const Row2& rs, const uint8_t* kt, const float (*w2)[64], int lane,
+                                             float (&sc)[2]) {
+  const int g = lane >> 4, col = lane & 15;
+  bf16x8 bf[4];
+  f32x4 acc0[4], acc1[4];
+  float p0[4], p1[4];                              // per-step parts of rows 0 and 1
+  load_bf2(kt, 0, g, col, bf);
+  mfma_row2(rs.a[0], bf, acc0);
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    mfma_row2(rs.a[1], bf, acc1);                  // row 1, step t
+    p0[t] = epi_row2(acc0, w2[0], g);              // row 0, step t (under row 1's MFMAs)
+    load_bf2(kt, t + 1, g, col, bf);
+    mfma_row2(rs.a[0], bf, acc0);                  // row 0, step t + 1
+    p1[t] = epi_row2(acc1, w2[1], g);              // row 1, step t (under row 0's MFMAs)
+  }
+  mfma_row2(rs.a[1], bf, acc1);                    // row 1, step 3
+  p0[3] = epi_row2(acc0, w2[0], g);
+  p1[3] = epi_row2(acc1, w2[1], g);
+  sc[0] = scatter4(p0[0], p0[1], p0[2], p0[3]);
+  sc[1] = scatter4(p1[0], p1[1], p1[2], p1[3]);
+}
+
+// TileDma for bf16 d = 128 without per-lane offset registers: each load's
+// offset is recomputed when it is issued (a few VALU ops per load), which keeps
+// the two-row kernel's loop free of spill reloads (a reload's vmcnt wait would
+// drain the tiles in flight).
+struct TileDma2 {
+  typedef Cfg<DT_BF16, 128, 64> C;
+  static constexpr int SPR = C::CPR + 1;                 // 16 data slots + 1 pad slot per row
+  static constexpr int NR = SPR;                         // loads per 64-row tile
+  static constexpr int NPW = (NR + kTopkWaves - 1) / kTopkWaves;
+  int wid, nload;
+  __device__ __forceinline__ explicit TileDma2(int wid_) : wid(wid_), nload((NR - wid_ + kTopkWaves - 1) / kTopkWaves) {}
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int tile, uint8_t* dst, int lane) const {
+    const uint32_t toff = (uint32_t)tile * (64 * C::ROWB);
+#pragma unroll
+    for (int m = 0; m < NPW; ++m) {
+      const int j = wid + kTopkWaves * m;
+      if (j < NR) {
+        const int q = 64 * j + lane;
+        const int row = q / SPR, part = q - row * SPR;
+        const uint32_t off = part < C::CPR ? (uint32_t)(row * C::ROWB + part * 16) : 0x80000000u;
+        lds_dma<16>(r, dst + j * 1024, off + toff);
+      }
+    }
+  }
+  __device__ __forceinline__ void wait_oldest(int younger) const {
+    const int n = younger * (nload == NPW ? NPW : NPW - 1);
+    switch (n) {
+#define DSA_VMW(c) case c: __builtin_amdgcn_s_waitcnt(0x0F70 | c); break;
+      DSA_VMW(1) DSA_VMW(2) DSA_VMW(3) DSA_VMW(4) DSA_VMW(5) DSA_VMW(6) DSA_VMW(7)
+      DSA_VMW(8) DSA_VMW(9) DSA_VMW(10) DSA_VMW(11) DSA_VMW(12) DSA_VMW(13) DSA_VMW(14) DSA_VMW(15)
+#undef DSA_VMW
+      default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    }
+  }
+};
+
+constexpr int kRowsPerWave2 = 2;
+constexpr int kRowsPerItem2 = kTopkWaves * kRowsPerWave2;
+
+__global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk2_kernel(IxParams p, uint32_t* work,
+                                                                                     uint32_t* cand) {
+  constexpr int TK = 64;
+  typedef Cfg<DT_BF16, 128, TK> C;
+  constexpr int STAGES = 3;
+  __shared__ __attribute__((aligned(16))) uint8_t ktile[STAGES][C::BUF_BYTES];
+  __shared__ uint32_t hist[kTopkWaves][256];
+  __shared__ __attribute__((aligned(16))) float w2s[kTopkWaves][2][64];
+  __shared__ int64_t s_item;
+
+  const int wid = wave_id(), lane = threadIdx.x & 63;
+  uint32_t* cu0 = cand + (((size_t)blockIdx.x * kTopkWaves + wid) * 2) * 2 * kCandCap;
+  uint32_t* cu1 = cu0 + 2 * kCandCap;
+  uint32_t* const cus[2] = {cu0, cu1};
+  const __amdgpu_buffer_rsrc_t crs0 = make_rsrc(cu0, 2u * kCandCap * 4u);
+  const __amdgpu_buffer_rsrc_t crs1 = make_rsrc(cu1, 2u * kCandCap * 4u);
+  const int64_t nrb = (p.rows + kRowsPerItem2 - 1) / kRowsPerItem2;
+  const int64_t total = nrb * p.batch;
+  const int k = p.topk;
+  const TileDma2 td(wid);
+
+  for (;;) {
+    if (threadIdx.x == 0) s_item = (int64_t)atomicAdd(work, 1u);
+    __syncthreads();
+    const int64_t item = s_item;
+    __syncthreads();
+    if (item >= total) break;
+    const int b = (int)(item % p.batch);
+    const int64_t rb = nrb - 1 - item / p.batch;                 // heaviest rows first
+    const int64_t rloc0 = rb * kRowsPerItem2;
+    const int64_t rlast = rloc0 + kRowsPerItem2 - 1 < p.rows ? rloc0 + kRowsPerItem2 - 1 : p.rows - 1;
+    const int64_t t_last = p.q_pos0 + p.row0 + rlast;
+    const int nkeys = (int)(t_last + 1 < p.n_k ? t_last + 1 : p.n_k);
+    const int ntiles = (nkeys + TK - 1) / TK;
+
+    bool vrow[2];
+    int tlim[2], first_cap[2];
+    int64_t gi[2];
+    Row2 rs;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t rloc = rloc0 + 2 * wid + j;
+      vrow[j] = rloc < p.rows;
+      const int64_t i = p.row0 + rloc;
+      const int t = vrow[j] ? (int)(p.q_pos0 + i) : -1;
+      tlim[j] = t < p.n_k - 1 ? t : p.n_k - 1;
+      first_cap[j] = tlim[j] < kShortRow ? kShortFirstCap : kCandCap;
+      gi[j] = (int64_t)b * p.n_q + i;
+      load_row2(p, gi[j], vrow[j], j, lane, rs, w2s[wid]);
+    }
+    settle_row2(rs);
+    const int tmax = tlim[0] > tlim[1] ? tlim[0] : tlim[1];
+    const uint8_t* kbase = (const uint8_t*)p.k + (int64_t)b * p.k_bs * C::ES;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (uint32_t)nkeys * C::ROWB);
+
+    int cnt[2] = {0, 0};
+    bool full[2] = {false, false}, strict[2] = {false, false};
+    uint32_t thr[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < STAGES - 1; ++i)
+      if (i < ntiles) td.load(krs, i, ktile[i], lane);
+    for (int it = 0; it < ntiles; ++it) {
+      const int ahead = ntiles - 1 - it;
+      td.wait_oldest(ahead < STAGES - 2 ? ahead : STAGES - 2);
+      tile_barrier();
+      if (it + STAGES - 1 < ntiles) td.load(krs, it + STAGES - 1, ktile[(it + STAGES - 1) % STAGES], lane);
+      const uint8_t* kt = ktile[it % STAGES];
+      if (it * TK <= tmax) {
+        float sc[2];
+        tile_scores2(rs, kt, w2s[wid], lane, sc);
+        const int s = it * TK + lane;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if (it * TK > tlim[j]) continue;
+          const uint32_t u = order_key(sc[j]);
+          if (cnt[j] + 64 > (full[j] ? kCandCap : first_cap[j])) {
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+            const Shrunk sh = wave_shrink(cus[j], cus[j] + kCandCap, cnt[j], k, hist[wid], lane);
+            cnt[j] = sh.n;
+            thr[j] = sh.thr;
+            strict[j] = sh.strict;
+            full[j] = true;
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+          }
+          const bool pr = s <= tlim[j] && (!full[j] || (strict[j] ? u > thr[j] : u >= thr[j]));
+          const uint64_t m = ballot(pr);
+          if (pr) {
+            const uint32_t d = (uint32_t)cnt[j] + lanes_below(m);
+            const __amdgpu_buffer_rsrc_t crs = j == 0 ? crs0 : crs1;
+            __builtin_amdgcn_raw_buffer_store_b32(u, crs, d * 4u, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32((uint32_t)s, crs, d * 4u, kCandCap * 4, 0);
+          }
+          cnt[j] += __builtin_popcountll(m);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (!vrow[j]) continue;
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+      uint32_t* cu = cus[j];
+      uint32_t* ci = cu + kCandCap;
+      int32_t* out = p.idx + gi[j] * (int64_t)k;
+      int nout;
+      if (cnt[j] > k) {
+        const ExactPick e = wave_select_exact(cu, cnt[j], k, hist[wid], lane);
+        nout = wave_keep(cu, ci, cnt[j], e.T, (int64_t)e.req, lane, out, k);
+        nout = nout < k ? nout : k;
+      } else {
+        for (int x = lane; x < cnt[j]; x += 64) out[x] = (int32_t)ci[x];
+        nout = cnt[j];
+      }
+      for (int x = nout + lane; x < k; x += 64) out[x] = -1;
+      lds_sync();
+    }
+  }
+}
+
 // ---------------------------------------------------------------- decode scan
 // The grid holds about two workgroups per CU (one round, no tail).  The G
 // workgroups of a row sweep its keys together in 256-key blocks: workgroup x
@@ -1049,6 +1321,16 @@ hipError_t launch_topk_dt(const IxParams& p, void* ws, hipStream_t s) {
   int64_t nb = persistent_blocks();
   if (nb > items) nb = items;
   dim3 grid((unsigned)nb);
+  if constexpr (DT == DT_BF16 && D == 128) {
+    if (p.heads > 32) {
+      const int64_t items2 = ((p.rows + kRowsPerItem2 - 1) / kRowsPerItem2) * p.batch;
+      int64_t nb2 = persistent_blocks();
+      if (nb2 > dsa_host::kTopkWaveSlots / kRowsPerItem2) nb2 = dsa_host::kTopkWaveSlots / kRowsPerItem2;
+      if (nb2 > items2) nb2 = items2;
+      hipLaunchKernelGGL(ix_topk2_kernel, dim3((unsigned)nb2), dim3(kTopkThreads), 0, s, p, work, cand);
+      return hipGetLastError();
+    }
+  }
   if (p.heads > 32) {
     hipLaunchKernelGGL((ix_topk_kernel<DT, D, 2>), grid, dim3(kTopkThreads), 0, s, p, work, cand);
   } else {
