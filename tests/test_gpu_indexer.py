@@ -106,6 +106,17 @@ def test_fused_prefill_small_heads_and_dims(dsa, dev):
         check_exact(dsa, ixi, 50)
 
 
+@pytest.mark.parametrize("heads", [33, 40, 50, 64])
+def test_fused_prefill_two_row_kernel_edges(dsa, dev, heads):
+    """bf16 d=128 with more than 32 heads runs two query rows per wave, eight rows
+    per workgroup: head counts that leave partial 16-head tiles, and row counts
+    (n_q = 333, 8 * 41 + 5) whose last workgroup has a wave with only its first
+    row valid."""
+    ixi = syn.indexer_inputs(B=2, n_q=333, H=heads, d=128, dtype=syn.BF16, values="int", w_dist="pm_pow2",
+                             seed=heads, device=dev)
+    check_exact(dsa, ixi, 100)
+
+
 def test_fused_prefill_signed_weights_and_offset(dsa, dev):
     """Signed w (negative heads) and a query window that starts at q_pos0 > 0
     (chunked prefill: the keys before the window are already cached)."""
