@@ -869,13 +869,6 @@ __global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk_kernel
 // 4g..4g+3 of the tile.  A wave owns two adjacent query rows, so every key
 // fragment read from LDS feeds both rows' MFMAs and a workgroup's staged tiles
 // serve eight rows.
-__device__ __forceinline__ float quad_sum2(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 struct Row2 {
   bf16x8 a[2][4][4];   // [row][head tile][K step]
 };
