@@ -862,62 +862,110 @@ __global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk_kernel
   }
 }
 
-// ---------------------------------------------------------------- fused, two rows per wave (bf16, d = 128)
-// v_mfma_f32_16x16x32_bf16 tiles: A = 16 heads of one query row, B = 16 keys
-// (K^T), both with lane (g = lane >> 4, c = lane & 15) holding row/column c and
-// K elements 8g..8g+7 of the 32-wide step; D lane (g, c) holds key c, heads
-// 4g..4g+3 of the tile.  A wave owns two adjacent query rows, so every key
-// fragment read from LDS feeds both rows' MFMAs and a workgroup's staged tiles
-// serve eight rows.
-struct Row2 {
-  bf16x8 a[2][4][4];   // [row][head tile][K step]
+// ---------------------------------------------------------------- fused, two rows per wave (d = 128)
+// 16x16 MFMA tiles: A = 16 heads of one query row, B = 16 keys (K^T), both with
+// lane (g = lane >> 4, c = lane & 15) holding row/column c and a quarter of the
+// K slice (bf16 v_mfma_f32_16x16x32_bf16: elements 8g..8g+7 of each 32-wide
+// step; fp8 v_mfma_scale_f32_16x16x128_f8f6f4: bytes 32g..32g+31 of the whole
+// 128-byte row); D lane (g, c) holds key c, heads 4g..4g+3 of the tile.  A wave
+// owns two adjacent query rows, so every key fragment read from LDS feeds both
+// rows' MFMAs and a workgroup's staged tiles serve eight rows.
+template <int DT>
+struct Frag2;
+template <>
+struct Frag2<DT_BF16> {
+  typedef bf16x8 T;
+  static constexpr int NKS = 4;          // 32-element K steps per 128-element row
+};
+template <>
+struct Frag2<DT_FP8> {
+  typedef i32x8 T;
+  static constexpr int NKS = 1;          // one 128-byte step
 };
 
-// q fragments of row j into registers; its head weights into the wave's LDS
-// table w2[j][0..64) (zero for heads >= H), read back by the epilogue with
-// broadcast loads (the lanes of one 16-lane group read the same 4 weights).
-__device__ __forceinline__ void load_row2(const IxParams& p, int64_t gi, bool valid, int j, int lane, Row2& rs,
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16(const typename Frag2<DT>::T& a, const typename Frag2<DT>::T& b, f32x4 c) {
+  if constexpr (DT == DT_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// This lane's K slice of step ks of one 128-element row at rowp (bytes).
+template <int DT>
+__device__ __forceinline__ typename Frag2<DT>::T load_frag2(const uint8_t* rowp, int ks, int g) {
+  if constexpr (DT == DT_BF16) {
+    return *(const bf16x8*)(rowp + 64 * ks + 16 * g);
+  } else {
+    const i32x4* q = (const i32x4*)(rowp + 32 * g);
+    const i32x4 lo = q[0], hi = q[1];
+    i32x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+  }
+}
+
+template <int DT>
+struct Row2 {
+  typename Frag2<DT>::T a[2][4][Frag2<DT>::NKS];   // [row][head tile][K step]
+};
+
+// q fragments of row j into registers; its epilogue weights (w, times the
+// query scale for fp8) into the wave's LDS table w2[j][0..64) (zero for heads
+// >= H), read back by the epilogue with broadcast loads (the lanes of one
+// 16-lane group read the same 4 weights).
+template <int DT>
+__device__ __forceinline__ void load_row2(const IxParams& p, int64_t gi, bool valid, int j, int lane, Row2<DT>& rs,
                                           float (*w2)[64]) {
+  typedef Cfg<DT, 128> C;
   const int g = lane >> 4, col = lane & 15;
-  const __bf16* qb = (const __bf16*)p.q;
-  w2[j][lane] = (valid && lane < p.heads) ? p.w[gi * p.heads + lane] : 0.f;
+  float cw = 0.f;
+  if (valid && lane < p.heads) {
+    cw = p.w[gi * p.heads + lane];
+    if constexpr (DT == DT_FP8) cw *= p.q_scale[gi * p.heads + lane];
+  }
+  w2[j][lane] = cw;
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
     const int head = 16 * h + col;
     if (valid && head < p.heads) {
-      const __bf16* rowp = qb + (gi * p.heads + head) * 128 + 8 * g;
+      const uint8_t* rowp = (const uint8_t*)p.q + (gi * p.heads + head) * (int64_t)C::ROWB;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) rs.a[j][h][ks] = *(const bf16x8*)(rowp + 32 * ks);
+      for (int ks = 0; ks < Frag2<DT>::NKS; ++ks) rs.a[j][h][ks] = load_frag2<DT>(rowp, ks, g);
     } else {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) rs.a[j][h][ks] = bf16x8{};
+      for (int ks = 0; ks < Frag2<DT>::NKS; ++ks) rs.a[j][h][ks] = typename Frag2<DT>::T{};
     }
   }
 }
 
-__device__ __forceinline__ void settle_row2(Row2& rs) {
+template <int DT>
+__device__ __forceinline__ void settle_row2(Row2<DT>& rs) {
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
+    for (int h = 0; h < 4; ++h)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(rs.a[j][h][ks]));
-    }
+      for (int ks = 0; ks < Frag2<DT>::NKS; ++ks) asm volatile("" : "+v"(rs.a[j][h][ks]));
 }
 
-// Scores of the 64 keys of an LDS tile for both rows: lane l gets key l.  The
-// rows are staggered by half a 16-key step so that each row's ReLU-w epilogue
-// runs under the other row's MFMAs: row 0 of step t+1 is multiplied while row 1
-// of step t is summed, with one row's accumulators in flight at a time.
-__device__ __forceinline__ void mfma_row2(const bf16x8 (&a)[4][4], const bf16x8 (&bf)[4], f32x4 (&acc)[4]) {
+// Scores of an LDS tile's keys for both rows: group q of 64 keys, lane l gets
+// key 64 q + l.  The rows are staggered by half a 16-key step so that each
+// row's ReLU-w epilogue runs under the other row's MFMAs: row 0 of step t+1 is
+// multiplied while row 1 of step t is summed, with one row's accumulators in
+// flight at a time.
+template <int DT>
+__device__ __forceinline__ void mfma_row2(const typename Frag2<DT>::T (&a)[4][Frag2<DT>::NKS],
+                                          const typename Frag2<DT>::T (&bf)[Frag2<DT>::NKS], f32x4 (&acc)[4]) {
 #pragma unroll
   for (int h = 0; h < 4; ++h) acc[h] = f32x4{};
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
+  for (int ks = 0; ks < Frag2<DT>::NKS; ++ks)
 #pragma unroll
-    for (int h = 0; h < 4; ++h) acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[h][ks], bf[ks], acc[h], 0, 0, 0);
+    for (int h = 0; h < 4; ++h) acc[h] = mfma16<DT>(a[h][ks], bf[ks], acc[h]);
 }
-// This lane's part of the head sum (its 16 heads) for key col of one step.
+// This lane's part of the head sum (its 16 heads) for key c of one step.
 __device__ __forceinline__ float epi_row2(const f32x4 (&acc)[4], const float* w, int g) {
   float pp = 0.f;
 #pragma unroll
@@ -928,7 +976,7 @@ __device__ __forceinline__ float epi_row2(const f32x4 (&acc)[4], const float* w,
   }
   return pp;
 }
-// Reduce-scatter of the four steps' parts over the four 16-lane groups: lane
+// Reduce-scatter of four steps' parts over the four 16-lane groups: lane
 // (g, c) ends with the full sum of step g, key 16 g + c, i.e. key `lane`.
 // v_permlane16_swap(x, y) swaps x's odd 16-lane rows with y's even rows, so
 // x + y then holds x's step in the even rows and y's in the odd rows, each
@@ -941,48 +989,59 @@ __device__ __forceinline__ float scatter4(float p0, float p1, float p2, float p3
   const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(sa), __float_as_uint(sb), false, false);
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);                 // row r: step r, all four rows
 }
-__device__ __forceinline__ void load_bf2(const uint8_t* kt, int t, int g, int col, bf16x8 (&bf)[4]) {
-  typedef Cfg<DT_BF16, 128> C;
-  const uint8_t* rowp = kt + (16 * t + col) * C::PITCH + 16 * g;
+template <int DT>
+__device__ __forceinline__ void load_bf2(const uint8_t* kt, int t, int g, int col,
+                                         typename Frag2<DT>::T (&bf)[Frag2<DT>::NKS]) {
+  typedef Cfg<DT, 128> C;
+  const uint8_t* rowp = kt + (16 * t + col) * C::PITCH;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) bf[ks] = *(const bf16x8*)(rowp + 64 * ks);
+  for (int ks = 0; ks < Frag2<DT>::NKS; ++ks) bf[ks] = load_frag2<DT>(rowp, ks, g);
 }
-__device__ __forceinline__ void tile_scores2(const Row2& rs, const uint8_t* kt, const float (*w2)[64], int lane,
-                                             float (&sc)[2]) {
+template <int DT, int NG>
+__device__ __forceinline__ void tile_scores2(const Row2<DT>& rs, const uint8_t* kt, const float (*w2)[64], int lane,
+                                             float (&sc)[NG][2]) {
+  constexpr int NS = 4 * NG;                       // 16-key steps per tile
   const int g = lane >> 4, col = lane & 15;
-  bf16x8 bf[4];
+  typename Frag2<DT>::T bf[Frag2<DT>::NKS];
   f32x4 acc0[4], acc1[4];
-  float p0[4], p1[4];                              // per-step parts of rows 0 and 1
-  load_bf2(kt, 0, g, col, bf);
-  mfma_row2(rs.a[0], bf, acc0);
+  float p0[NS], p1[NS];                            // per-step parts of rows 0 and 1
+  load_bf2<DT>(kt, 0, g, col, bf);
+  mfma_row2<DT>(rs.a[0], bf, acc0);
 #pragma unroll
-  for (int t = 0; t < 3; ++t) {
-    mfma_row2(rs.a[1], bf, acc1);                  // row 1, step t
+  for (int t = 0; t < NS - 1; ++t) {
+    mfma_row2<DT>(rs.a[1], bf, acc1);              // row 1, step t
     p0[t] = epi_row2(acc0, w2[0], g);              // row 0, step t (under row 1's MFMAs)
-    load_bf2(kt, t + 1, g, col, bf);
-    mfma_row2(rs.a[0], bf, acc0);                  // row 0, step t + 1
+    load_bf2<DT>(kt, t + 1, g, col, bf);
+    mfma_row2<DT>(rs.a[0], bf, acc0);              // row 0, step t + 1
     p1[t] = epi_row2(acc1, w2[1], g);              // row 1, step t (under row 0's MFMAs)
   }
-  mfma_row2(rs.a[1], bf, acc1);                    // row 1, step 3
-  p0[3] = epi_row2(acc0, w2[0], g);
-  p1[3] = epi_row2(acc1, w2[1], g);
-  sc[0] = scatter4(p0[0], p0[1], p0[2], p0[3]);
-  sc[1] = scatter4(p1[0], p1[1], p1[2], p1[3]);
+  mfma_row2<DT>(rs.a[1], bf, acc1);                // row 1, last step
+  p0[NS - 1] = epi_row2(acc0, w2[0], g);
+  p1[NS - 1] = epi_row2(acc1, w2[1], g);
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    sc[q][0] = scatter4(p0[4 * q], p0[4 * q + 1], p0[4 * q + 2], p0[4 * q + 3]);
+    sc[q][1] = scatter4(p1[4 * q], p1[4 * q + 1], p1[4 * q + 2], p1[4 * q + 3]);
+  }
 }
 
-// TileDma for bf16 d = 128 without per-lane offset registers: each load's
-// offset is recomputed when it is issued (a few VALU ops per load), which keeps
-// the two-row kernel's loop free of spill reloads (a reload's vmcnt wait would
-// drain the tiles in flight).
+// Tile staging of the two-row kernel: the TileDma loads without per-lane offset
+// registers (each load's offset is recomputed when it is issued, a few VALU ops):
+// a spilled offset reloaded inside the tile loop would wait for every load in
+// flight, the staged tiles included.
+template <int DT, int TK>
 struct TileDma2 {
-  typedef Cfg<DT_BF16, 128, 64> C;
-  static constexpr int SPR = C::CPR + 1;                 // 16 data slots + 1 pad slot per row
-  static constexpr int NR = SPR;                         // loads per 64-row tile
-  static constexpr int NPW = (NR + kTopkWaves - 1) / kTopkWaves;
+  typedef Cfg<DT, 128, TK> C;
+  static constexpr int SPR = C::CPR + 1;                 // data slots + 1 pad slot per row
+  static constexpr int NGR = TK / 64;
+  static constexpr int NR = NGR * SPR;                   // row loads per tile
+  static constexpr int NI = NR + (DT == DT_FP8 ? NGR : 0);   // + key-scale loads
+  static constexpr int NPW = (NI + kTopkWaves - 1) / kTopkWaves;
   int wid, nload;
-  __device__ __forceinline__ explicit TileDma2(int wid_) : wid(wid_), nload((NR - wid_ + kTopkWaves - 1) / kTopkWaves) {}
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int tile, uint8_t* dst, int lane) const {
-    const uint32_t toff = (uint32_t)tile * (64 * C::ROWB);
+  __device__ __forceinline__ explicit TileDma2(int wid_) : wid(wid_), nload((NI - wid_ + kTopkWaves - 1) / kTopkWaves) {}
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, __amdgpu_buffer_rsrc_t sr, int tile, uint8_t* dst,
+                                       int lane) const {
+    const uint32_t toff = (uint32_t)tile * (TK * C::ROWB);
 #pragma unroll
     for (int m = 0; m < NPW; ++m) {
       const int j = wid + kTopkWaves * m;
@@ -991,6 +1050,9 @@ struct TileDma2 {
         const int row = q / SPR, part = q - row * SPR;
         const uint32_t off = part < C::CPR ? (uint32_t)(row * C::ROWB + part * 16) : 0x80000000u;
         lds_dma<16>(r, dst + j * 1024, off + toff);
+      } else if (DT == DT_FP8 && j < NI) {
+        const int q = j - NR;
+        lds_dma<4>(sr, dst + C::TILE_BYTES + 256 * q, (uint32_t)(tile * TK + 64 * q + lane) * 4u);
       }
     }
   }
@@ -1009,10 +1071,13 @@ struct TileDma2 {
 constexpr int kRowsPerWave2 = 2;
 constexpr int kRowsPerItem2 = kTopkWaves * kRowsPerWave2;
 
+template <int DT>
 __global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk2_kernel(IxParams p, uint32_t* work,
                                                                                      uint32_t* cand) {
-  constexpr int TK = 64;
-  typedef Cfg<DT_BF16, 128, TK> C;
+  // 128-key tiles where three buffers fit two workgroups per CU (fp8), else 64
+  constexpr int TK = Cfg<DT, 128, 128>::BUF_BYTES <= 24576 ? 128 : 64;
+  constexpr int NG = TK / 64;
+  typedef Cfg<DT, 128, TK> C;
   constexpr int STAGES = 3;
   __shared__ __attribute__((aligned(16))) uint8_t ktile[STAGES][C::BUF_BYTES];
   __shared__ uint32_t hist[kTopkWaves][256];
@@ -1028,7 +1093,7 @@ __global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk2_kerne
   const int64_t nrb = (p.rows + kRowsPerItem2 - 1) / kRowsPerItem2;
   const int64_t total = nrb * p.batch;
   const int k = p.topk;
-  const TileDma2 td(wid);
+  const TileDma2<DT, TK> td(wid);
 
   for (;;) {
     if (threadIdx.x == 0) s_item = (int64_t)atomicAdd(work, 1u);
@@ -1047,7 +1112,7 @@ __global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk2_kerne
     bool vrow[2];
     int tlim[2], first_cap[2];
     int64_t gi[2];
-    Row2 rs;
+    Row2<DT> rs;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int64_t rloc = rloc0 + 2 * wid + j;
@@ -1057,51 +1122,64 @@ __global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk2_kerne
       tlim[j] = t < p.n_k - 1 ? t : p.n_k - 1;
       first_cap[j] = tlim[j] < kShortRow ? kShortFirstCap : kCandCap;
       gi[j] = (int64_t)b * p.n_q + i;
-      load_row2(p, gi[j], vrow[j], j, lane, rs, w2s[wid]);
+      load_row2<DT>(p, gi[j], vrow[j], j, lane, rs, w2s[wid]);
     }
-    settle_row2(rs);
+    settle_row2<DT>(rs);
     const int tmax = tlim[0] > tlim[1] ? tlim[0] : tlim[1];
     const uint8_t* kbase = (const uint8_t*)p.k + (int64_t)b * p.k_bs * C::ES;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (uint32_t)nkeys * C::ROWB);
+    // fp8 key scales (unused for bf16: an empty range)
+    const __amdgpu_buffer_rsrc_t srs =
+        make_rsrc(DT == DT_FP8 ? (const void*)(p.k_scale + (int64_t)b * p.ks_bs) : (const void*)kbase,
+                  DT == DT_FP8 ? (uint32_t)nkeys * 4u : 0u);
 
     int cnt[2] = {0, 0};
     bool full[2] = {false, false}, strict[2] = {false, false};
     uint32_t thr[2] = {0u, 0u};
 #pragma unroll
     for (int i = 0; i < STAGES - 1; ++i)
-      if (i < ntiles) td.load(krs, i, ktile[i], lane);
+      if (i < ntiles) td.load(krs, srs, i, ktile[i], lane);
     for (int it = 0; it < ntiles; ++it) {
       const int ahead = ntiles - 1 - it;
       td.wait_oldest(ahead < STAGES - 2 ? ahead : STAGES - 2);
       tile_barrier();
-      if (it + STAGES - 1 < ntiles) td.load(krs, it + STAGES - 1, ktile[(it + STAGES - 1) % STAGES], lane);
+      if (it + STAGES - 1 < ntiles) td.load(krs, srs, it + STAGES - 1, ktile[(it + STAGES - 1) % STAGES], lane);
       const uint8_t* kt = ktile[it % STAGES];
       if (it * TK <= tmax) {
-        float sc[2];
-        tile_scores2(rs, kt, w2s[wid], lane, sc);
-        const int s = it * TK + lane;
+        float sc[NG][2];
+        tile_scores2<DT, NG>(rs, kt, w2s[wid], lane, sc);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          if (it * TK > tlim[j]) continue;
-          const uint32_t u = order_key(sc[j]);
-          if (cnt[j] + 64 > (full[j] ? kCandCap : first_cap[j])) {
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-            const Shrunk sh = wave_shrink(cus[j], cus[j] + kCandCap, cnt[j], k, hist[wid], lane);
-            cnt[j] = sh.n;
-            thr[j] = sh.thr;
-            strict[j] = sh.strict;
-            full[j] = true;
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        for (int q = 0; q < NG; ++q) {
+          const int s0 = it * TK + 64 * q;
+          if (s0 > tmax) break;
+          const int s = s0 + lane;
+          float kscale = 1.f;
+          if constexpr (DT == DT_FP8) kscale = *(const float*)(kt + C::TILE_BYTES + (64 * q + lane) * 4);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            if (s0 > tlim[j]) continue;
+            float v = sc[q][j];
+            if constexpr (DT == DT_FP8) v *= kscale;
+            const uint32_t u = order_key(v);
+            if (cnt[j] + 64 > (full[j] ? kCandCap : first_cap[j])) {
+              __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+              const Shrunk sh = wave_shrink(cus[j], cus[j] + kCandCap, cnt[j], k, hist[wid], lane);
+              cnt[j] = sh.n;
+              thr[j] = sh.thr;
+              strict[j] = sh.strict;
+              full[j] = true;
+              __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+            }
+            const bool pr = s <= tlim[j] && (!full[j] || (strict[j] ? u > thr[j] : u >= thr[j]));
+            const uint64_t m = ballot(pr);
+            if (pr) {
+              const uint32_t d = (uint32_t)cnt[j] + lanes_below(m);
+              const __amdgpu_buffer_rsrc_t crs = j == 0 ? crs0 : crs1;
+              __builtin_amdgcn_raw_buffer_store_b32(u, crs, d * 4u, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b32((uint32_t)s, crs, d * 4u, kCandCap * 4, 0);
+            }
+            cnt[j] += __builtin_popcountll(m);
           }
-          const bool pr = s <= tlim[j] && (!full[j] || (strict[j] ? u > thr[j] : u >= thr[j]));
-          const uint64_t m = ballot(pr);
-          if (pr) {
-            const uint32_t d = (uint32_t)cnt[j] + lanes_below(m);
-            const __amdgpu_buffer_rsrc_t crs = j == 0 ? crs0 : crs1;
-            __builtin_amdgcn_raw_buffer_store_b32(u, crs, d * 4u, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b32((uint32_t)s, crs, d * 4u, kCandCap * 4, 0);
-          }
-          cnt[j] += __builtin_popcountll(m);
         }
       }
     }
@@ -1314,13 +1392,13 @@ hipError_t launch_topk_dt(const IxParams& p, void* ws, hipStream_t s) {
   int64_t nb = persistent_blocks();
   if (nb > items) nb = items;
   dim3 grid((unsigned)nb);
-  if constexpr (DT == DT_BF16 && D == 128) {
+  if constexpr (D == 128) {
     if (p.heads > 32) {
       const int64_t items2 = ((p.rows + kRowsPerItem2 - 1) / kRowsPerItem2) * p.batch;
       int64_t nb2 = persistent_blocks();
       if (nb2 > dsa_host::kTopkWaveSlots / kRowsPerItem2) nb2 = dsa_host::kTopkWaveSlots / kRowsPerItem2;
       if (nb2 > items2) nb2 = items2;
-      hipLaunchKernelGGL(ix_topk2_kernel, dim3((unsigned)nb2), dim3(kTopkThreads), 0, s, p, work, cand);
+      hipLaunchKernelGGL(ix_topk2_kernel<DT>, dim3((unsigned)nb2), dim3(kTopkThreads), 0, s, p, work, cand);
       return hipGetLastError();
     }
   }
