@@ -784,7 +784,9 @@ __global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk_kernel
     const int64_t rlast = rloc0 + kTopkWaves - 1 < p.rows ? rloc0 + kTopkWaves - 1 : p.rows - 1;
     const int64_t t_last = p.q_pos0 + p.row0 + rlast;
     const int nkeys = (int)(t_last + 1 < p.n_k ? t_last + 1 : p.n_k);
-    const int ntiles = (nkeys + TK - 1) / TK;
+    // every row of the item selects all its positions: no scores needed (the
+    // item's key count is the same for all waves, so the barriers still match)
+    const int ntiles = nkeys <= k ? 0 : (nkeys + TK - 1) / TK;
     const int tlim = t < p.n_k - 1 ? t : p.n_k - 1;             // last candidate position
     const int first_cap = tlim < kShortRow ? kShortFirstCap : kCandCap;
     const int64_t gi = (int64_t)b * p.n_q + i;
@@ -848,7 +850,10 @@ __global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk_kernel
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
       int32_t* out = p.idx + gi * (int64_t)k;
       int nout;
-      if (cnt > k) {
+      if (tlim < k) {                                            // all of 0..t
+        for (int j = lane; j <= tlim; j += 64) out[j] = j;
+        nout = tlim + 1;
+      } else if (cnt > k) {
         const ExactPick e = wave_select_exact(cu, cnt, k, hist[wid], lane);
         nout = wave_keep(cu, ci, cnt, e.T, (int64_t)e.req, lane, out, k);
         nout = nout < k ? nout : k;
@@ -1107,7 +1112,7 @@ __global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk2_kerne
     const int64_t rlast = rloc0 + kRowsPerItem2 - 1 < p.rows ? rloc0 + kRowsPerItem2 - 1 : p.rows - 1;
     const int64_t t_last = p.q_pos0 + p.row0 + rlast;
     const int nkeys = (int)(t_last + 1 < p.n_k ? t_last + 1 : p.n_k);
-    const int ntiles = (nkeys + TK - 1) / TK;
+    const int ntiles = nkeys <= k ? 0 : (nkeys + TK - 1) / TK;   // as in ix_topk_kernel
 
     bool vrow[2];
     int tlim[2], first_cap[2];
@@ -1191,7 +1196,10 @@ __global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk2_kerne
       uint32_t* ci = cu + kCandCap;
       int32_t* out = p.idx + gi[j] * (int64_t)k;
       int nout;
-      if (cnt[j] > k) {
+      if (tlim[j] < k) {
+        for (int x = lane; x <= tlim[j]; x += 64) out[x] = x;
+        nout = tlim[j] + 1;
+      } else if (cnt[j] > k) {
         const ExactPick e = wave_select_exact(cu, cnt[j], k, hist[wid], lane);
         nout = wave_keep(cu, ci, cnt[j], e.T, (int64_t)e.req, lane, out, k);
         nout = nout < k ? nout : k;

@@ -125,6 +125,20 @@ def test_fused_prefill_signed_weights_and_offset(dsa, dev):
     check_exact(dsa, ixi, 256)
 
 
+@pytest.mark.parametrize("H_,d,dt", [(64, 128, syn.BF16), (64, 128, syn.FP8), (16, 64, syn.BF16)])
+def test_fused_prefill_rows_shorter_than_k(dsa, dev, H_, d, dt):
+    """Row blocks whose every row has at most k candidates write 0..t without
+    scoring; the block that straddles t = k - 1 scores for its longer rows only.
+    Then a key cache shorter than k, with query rows past its end (each of those
+    selects all n_k keys).  Two-row kernel (64 heads, d = 128) and one-row kernel."""
+    ixi = syn.indexer_inputs(B=2, n_q=700, H=H_, d=d, dtype=dt, values="int", w_dist="pow2", seed=H_ + d + 5,
+                             device=dev)
+    check_exact(dsa, ixi, 517)
+    ixi = syn.indexer_inputs(B=2, n_q=90, n_k=70, H=H_, d=d, dtype=dt, values="int", w_dist="pow2",
+                             seed=H_ + d + 6, device=dev)
+    check_exact(dsa, ixi, 128)
+
+
 # --------------------------------------------------------------------------- materialised paths
 @pytest.mark.parametrize("dtype", [syn.BF16, syn.FP8])
 def test_indexer_scores_window(dsa, dev, dtype):
