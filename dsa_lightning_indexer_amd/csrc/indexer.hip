@@ -1151,8 +1151,15 @@ __global__ __launch_bounds__(kTopkThreads, kTopkBlocksPerCu) void ix_topk2_kerne
       if (it + STAGES - 1 < ntiles) td.load(krs, srs, it + STAGES - 1, ktile[(it + STAGES - 1) % STAGES], lane);
       const uint8_t* kt = ktile[it % STAGES];
       if (it * TK <= tmax) {
+        // Scores at normal wave priority, everything else (appends, compactions, the
+        // next tile's wait, barrier and DMA issue, the final select, the next row
+        // block's set-up) raised: the SIMD's other wave is then mostly issuing MFMAs,
+        // each of which keeps the matrix core busy for 16 (bf16) or 32 (fp8) cycles.
+        // Measured 0.5-2% faster; the order of the work itself is unchanged.
+        __builtin_amdgcn_s_setprio(0);
         float sc[NG][2];
         tile_scores2<DT, NG>(rs, kt, w2s[wid], lane, sc);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int q = 0; q < NG; ++q) {
           const int s0 = it * TK + 64 * q;
