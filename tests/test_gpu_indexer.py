@@ -2,6 +2,8 @@
 
 Integer-valued inputs: indices bit-exact, scores exactly equal.  Float inputs:
 scores within 1e-3 * A and the index-set tie-window rule (see helpers)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -137,6 +139,50 @@ def test_fused_prefill_rows_shorter_than_k(dsa, dev, H_, d, dt):
     ixi = syn.indexer_inputs(B=2, n_q=90, n_k=70, H=H_, d=d, dtype=dt, values="int", w_dist="pow2",
                              seed=H_ + d + 6, device=dev)
     check_exact(dsa, ixi, 128)
+
+
+@pytest.mark.parametrize("k", [1, 2, 7])
+def test_small_k_with_ties(dsa, dev, k):
+    """k far below the tile width on integer-valued inputs (many tied scores, so
+    the lower-position tie-break decides): two-row kernel (bf16 and fp8, through
+    the candidate compaction at L = 9000), one-row kernel, and the few-row decode
+    select over a 5000-key cache."""
+    ixi = syn.indexer_inputs(B=1, n_q=9000, dtype=syn.BF16, values="int", w_dist="pow2", seed=40 + k, device=dev)
+    check_exact(dsa, ixi, k, rows=sample_rows(9000, k, seed=k))
+    ixi = syn.indexer_inputs(B=2, n_q=333, dtype=syn.FP8, values="int", w_dist="pm_pow2", seed=50 + k, device=dev)
+    check_exact(dsa, ixi, k)
+    ixi = syn.indexer_inputs(B=2, n_q=333, H=16, d=64, dtype=syn.BF16, values="int", w_dist="pow2", seed=60 + k,
+                             device=dev)
+    check_exact(dsa, ixi, k)
+    ixi = syn.indexer_inputs(B=3, n_q=1, n_k=5000, q_pos0=4999, dtype=syn.FP8, values="int", w_dist="pow2",
+                             seed=70 + k, device=dev)
+    check_exact(dsa, ixi, k)
+
+
+def _periodic_keys(ixi, period):
+    """The same inputs with key s replaced by key s mod period (and its scale):
+    every score recurs down the row, so the Top-k is decided by position."""
+    n_k = ixi.k.shape[1]
+    src = torch.arange(n_k, device=ixi.k.device) % period
+    ks = None if ixi.k_scale is None else ixi.k_scale[:, src].contiguous()
+    return dataclasses.replace(ixi, k=ixi.k[:, src].contiguous(), k_scale=ks)
+
+
+@pytest.mark.parametrize("dtype", [syn.BF16, syn.FP8])
+@pytest.mark.parametrize("k", [1, 2, 7, 100])
+def test_repeated_keys_tie_break(dsa, dev, dtype, k):
+    """Keys repeating with period 37: each row's best scores occur at several
+    positions and only the lowest ones may be selected.  Rows long enough to pass
+    the candidate compaction (L = 9000) and a decode row over 5000 keys."""
+    ixi = _periodic_keys(syn.indexer_inputs(B=1, n_q=9000, dtype=dtype, values="int", w_dist="pm_pow2",
+                                            seed=80 + k, device=dev), 37)
+    got = check_exact(dsa, ixi, k, rows=sample_rows(9000, k, seed=k))
+    # the best key pattern occurs at least k times below position 37 k, and ties go
+    # to the lower position: a long row selects nothing at or above 37 k
+    assert got[0, 8999, :k].max() < 37 * k
+    ixi = _periodic_keys(syn.indexer_inputs(B=2, n_q=1, n_k=5000, q_pos0=4999, dtype=dtype, values="int",
+                                            w_dist="pm_pow2", seed=90 + k, device=dev), 37)
+    check_exact(dsa, ixi, k)
 
 
 # --------------------------------------------------------------------------- materialised paths
