@@ -124,7 +124,7 @@ def test_decode_stack_fsss(dsa, dev):
 
 @pytest.mark.parametrize("retention", ["1/4", "1/8"])
 def test_searched_47_layer_pattern_on_gpu(dsa, dev, retention):
-    """A searched 47-layer sharing pattern ([DSA-NOTES] Appendix B) through the
+    """A searched 47-layer sharing pattern ([IC-SUMMARY] Appendix B) through the
     driver: every F layer's index tensor is bit-exact against the oracle on
     integer inputs, every layer attends with the tensor of its source layer
     (compared on sampled rows), and no S layer gets indexer inputs."""

@@ -319,16 +319,18 @@ def test_pattern_rules():
 
 
 def test_searched_patterns_from_the_page():
-    """[DSA-NOTES] Appendix B: the searched 47-layer patterns keep 24, 12 and 7 F
-    layers; the driver inputs match the printed strings (the 1/8 one with its
-    extra trailing S dropped) and every one starts with an F layer."""
+    """[IC-SUMMARY] Appendix B: the searched 47-layer patterns keep 24, 12 and 7 F
+    layers; the driver inputs are the printed strings, 47 characters each, and
+    every one starts with an F layer.  The 1/8 pattern has its F layers at
+    1, 5, 14, 18, 24, 29 and 38 (1-based), as printed."""
     g = gold("searched_patterns.json")
+    assert [i + 1 for i, c in enumerate(g["patterns_as_printed"]["1/8"]) if c == "F"] == \
+        g["f_positions_1based"]["1/8"] == [1, 5, 14, 18, 24, 29, 38]
     for r, text in g["patterns_as_printed"].items():
         used = syn.SEARCHED_PATTERNS_47[r]
-        assert len(used) == g["n_layers"]
-        assert used == text[:g["n_layers"]]
-        assert text[g["n_layers"]:] in ("", "S")
-        assert used.count("F") == text.count("F") == g["f_counts"][r]
+        assert len(text) == len(used) == g["n_layers"] == 47
+        assert used == text
+        assert used.count("F") == g["f_counts"][r]
         src = oracle.source_layers(used)
         assert src[0] == 1 and None not in src
         # an S layer's source is the nearest F layer before it
