@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(HERE, "libdsa.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m dsa_lightning_indexer_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python dsa_lightning_indexer_amd/build.py` "
         "(there is no fallback implementation)")
 
 LIB = ctypes.CDLL(LIB_PATH)
@@ -111,9 +111,32 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _dense(name, t):
+    """The kernels read these tensors as dense row-major arrays."""
+    if t is not None and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (got strides {tuple(t.stride())} for shape {tuple(t.shape)})")
+
+
+def _rows(name, t, row):
+    """Tensors passed with a batch stride: every dimension after the batch one must
+    be dense (rows of `row` elements back to back); the batch stride is free."""
+    if t is None:
+        return
+    expect = 1
+    for dim in range(t.dim() - 1, 0, -1):
+        if t.shape[dim] != 1 and t.stride(dim) != expect:
+            raise ValueError(f"{name} must be dense after its batch dimension (rows of {row} elements); "
+                             f"got strides {tuple(t.stride())} for shape {tuple(t.shape)}")
+        expect *= t.shape[dim]
+
+
 def indexer_args(q, k, w, q_scale=None, k_scale=None, q_pos0=0):
     """q [B, n_q, H, d], k [B, n_k, d] (rows dense, any batch stride), w [B, n_q, H] fp32."""
     B, n_q, H, d = q.shape
+    for name, t in (("q", q), ("w", w), ("q_scale", q_scale)):
+        _dense(name, t)
+    _rows("k", k, d)
+    _rows("k_scale", k_scale, 1)
     a = IndexerArgs()
     a.dtype = dtype_code(q)
     a.batch, a.n_q, a.n_k, a.heads, a.dim = B, n_q, k.shape[1], H, d
@@ -127,6 +150,12 @@ def indexer_args(q, k, w, q_scale=None, k_scale=None, q_pos0=0):
 def sparse_attn_args(q, kv, idx, scale, out, v=None, d_v=None):
     """q [B, n_q, H, d_qk], kv [B, n_k, G, d_qk], idx [B, n_q, topk] int32, out [B, n_q, H, d_v]."""
     B, n_q, H, d_qk = q.shape
+    for name, t in (("q", q), ("idx", idx)):
+        _dense(name, t)
+    if out is not None and out.numel() > 0:
+        _dense("out", out)
+    _rows("kv", kv, d_qk)
+    _rows("v", v, None if v is None else v.shape[-1])
     a = SparseAttnArgs()
     a.dtype = dtype_code(q)
     a.batch, a.n_q, a.n_k, a.heads, a.kv_heads, a.d_qk = B, n_q, kv.shape[1], H, kv.shape[2], d_qk

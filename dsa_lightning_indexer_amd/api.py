@@ -130,6 +130,8 @@ def indexer_distill(q, k, w, idx, teachers, *, q_pos0=0):
     B, n_q, H, d = q.shape
     n_k = k.shape[1]
     r, topk = teachers.shape[0], idx.shape[2]
+    L._dense("idx", idx)
+    L._dense("teachers", teachers)
     dev = q.device
     out = dict(loss=torch.empty((B, n_q), dtype=torch.float32, device=dev),
                delta=torch.empty((B, n_q, topk), dtype=torch.float32, device=dev),
@@ -151,6 +153,8 @@ def row_cosine(a, b, *, row_cos=None, mean=None):
     flattened).  Returns (row_cos fp32 [rows], mean float64 [1])."""
     rows = a.shape[0]
     width = a[0].numel() if rows else 0
+    L._dense("a", a)
+    L._dense("b", b)
     if row_cos is None:
         row_cos = torch.empty(rows, dtype=torch.float32, device=a.device)
     if mean is None:

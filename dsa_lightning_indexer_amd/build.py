@@ -1,6 +1,6 @@
 """Build libdsa.so (all HIP kernels + the C ABI) in-tree for gfx950.
 
-    python -m dsa_lightning_indexer_amd.build
+    python dsa_lightning_indexer_amd/build.py      (or __graft_entry__.build())
 """
 import os
 import subprocess
@@ -17,7 +17,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["select.hip", "select_few.hip", "indexer.hip", "sparse_attn.hip", "overlap.hip", "distill.hip", "similarity.hip",
            "pattern_search.cpp", "api.cpp"]
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Werror", "-Wno-unused-function",
     # keep the compiler from emitting packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

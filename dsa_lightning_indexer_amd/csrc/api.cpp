@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <climits>
 #include <cstring>
 #include <string>
 
@@ -102,6 +103,26 @@ size_t topk_ws(const dsa_indexer_args* a, const float* scores) {
   return 0;
 }
 
+// Limits of the kernels the chosen Top-k path launches.  Every caller that
+// scores an F layer (dsa_topk, indexcache_forward, dsa_similarity_matrix) runs
+// this before enqueueing anything.
+dsa_status check_topk_path(const dsa_indexer_args* a, const float* scores) {
+  const TopkPath path = topk_path(a, scores);
+  if (path != PATH_FUSED) {
+    // the materialised-score selects keep per-chunk state for at most this many scores per row
+    if (a->n_k > (int32_t)dsa_host::kSelectMaxRow)
+      return fail(DSA_ERR_UNSUPPORTED, "this Top-k path handles rows of at most %d scores", dsa_host::kSelectMaxRow);
+    return DSA_OK;
+  }
+  // the fused kernels address one batch's keys with 32-bit byte offsets and
+  // hold query positions in 32-bit integers
+  if ((int64_t)a->n_k * a->dim * (a->dtype == DSA_BF16 ? 2 : 1) >= (int64_t)1 << 31)
+    return fail(DSA_ERR_UNSUPPORTED, "fused indexer+Top-k needs n_k * dim * element size < 2^31 bytes");
+  if (a->q_pos0 + a->n_q > (int64_t)INT32_MAX)
+    return fail(DSA_ERR_UNSUPPORTED, "fused indexer+Top-k needs q_pos0 + n_q <= 2^31 - 1");
+  return DSA_OK;
+}
+
 dsa_status check_topk(const dsa_indexer_args* a, const float* scores, int32_t k, const int32_t* idx,
                       const void* ws, size_t ws_bytes) {
   dsa_status st = check_indexer_shape(a);
@@ -115,11 +136,8 @@ dsa_status check_topk(const dsa_indexer_args* a, const float* scores, int32_t k,
     st = check_indexer_data(a);
     if (st != DSA_OK) return st;
   }
-  if (topk_path(a, scores) != PATH_FUSED && a->n_k > (int32_t)dsa_host::kSelectMaxRow)
-    return fail(DSA_ERR_UNSUPPORTED, "this Top-k path handles rows of at most %d scores", dsa_host::kSelectMaxRow);
-  // the fused kernel addresses one batch's keys with 32-bit byte offsets
-  if (topk_path(a, scores) == PATH_FUSED && (int64_t)a->n_k * a->dim * (a->dtype == DSA_BF16 ? 2 : 1) >= (int64_t)1 << 31)
-    return fail(DSA_ERR_UNSUPPORTED, "fused indexer+Top-k needs n_k * dim * element size < 2^31 bytes");
+  st = check_topk_path(a, scores);
+  if (st != DSA_OK) return st;
   const size_t need = topk_ws(a, scores);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
@@ -283,6 +301,7 @@ static dsa_status check_forward(const char* pattern, int32_t n, const dsa_layer*
       src = l;
       dsa_status st = check_indexer_shape(&L.ix);
       if (st == DSA_OK) st = check_indexer_data(&L.ix);
+      if (st == DSA_OK) st = check_topk_path(&L.ix, nullptr);
       if (st != DSA_OK) return fail(st, "layer %d (F): %s", l, g_last_error.c_str());
       if (!L.idx_out || !aligned(L.idx_out, 4)) return fail(DSA_ERR_INVALID, "layer %d (F): idx_out NULL/misaligned", l);
       const size_t w = topk_ws(&L.ix, nullptr);
@@ -397,6 +416,7 @@ static dsa_status check_similarity(int32_t n, const dsa_layer* layers, int32_t k
     const dsa_layer& L = layers[l];
     dsa_status st = check_indexer_shape(&L.ix);
     if (st == DSA_OK) st = check_indexer_data(&L.ix);
+    if (st == DSA_OK) st = check_topk_path(&L.ix, nullptr);
     if (st != DSA_OK) return fail(st, "layer %d: %s", l, g_last_error.c_str());
     if (!sizing && (!L.idx_out || !aligned(L.idx_out, 4)))
       return fail(DSA_ERR_INVALID, "layer %d: idx_out NULL/misaligned", l);

@@ -230,3 +230,72 @@ def test_similarity_matrix_validation_and_workspace():
         a.sa.out = None                                     # attention outputs live in the workspace
         a.sa.idx = None
     assert L.dsa_similarity_matrix_workspace_size(3, free, 16) == need
+
+
+def one_f_layer(ixa, sa_rows=None):
+    """A one-layer pattern "F" whose attention matches the indexer's rows."""
+    arr = (L.Layer * 1)()
+    arr[0].ix = ixa
+    arr[0].idx_out = FAKE
+    arr[0].sa = sa(batch=ixa.batch, n_q=ixa.n_q, n_k=ixa.n_k, topk=16)
+    return arr
+
+
+@pytest.mark.parametrize("kw", [
+    # decode-shaped layer (scan + few-row select) longer than the select's row limit
+    dict(batch=8, n_q=1, n_k=4 * 1024 * 1024 + 1, q_pos0=4 * 1024 * 1024, dtype=L.DSA_FP8_E4M3, q_scale=FAKE,
+         k_scale=FAKE),
+    # fused prefill layer whose keys span 2^31 bytes (32-bit buffer offsets)
+    dict(n_q=4096, n_k=1 << 23),
+    # fused prefill layer whose last query position does not fit an int32
+    dict(n_q=4096, n_k=4096, q_pos0=(1 << 31) - 100),
+])
+def test_driver_applies_the_topk_path_limits(kw):
+    """Every F layer of indexcache_forward and dsa_similarity_matrix goes through
+    the same path limits as dsa_topk, before anything is enqueued."""
+    a = ix(**kw)
+    assert topk_status(a, k=16, ws=FAKE, ws_bytes=1 << 40) == 2
+    arr = one_f_layer(a)
+    assert L.indexcache_forward_c(b"F", 1, arr, 16, None, FAKE, 1 << 40, None) == 2
+    assert b"layer 0" in L.dsa_last_error()
+    assert L.indexcache_forward_workspace_size(b"F", 1, arr, 16) == 0
+    assert L.dsa_similarity_matrix(1, arr, 16, FAKE, FAKE, 1 << 40, None) == 2
+    assert L.dsa_similarity_matrix_workspace_size(1, arr, 16) == 0
+
+
+def test_driver_accepts_the_largest_fused_layer():
+    """Just inside the limits: validation passes and only the workspace is missing."""
+    arr = one_f_layer(ix(n_q=4096, n_k=(1 << 23) - 8, q_pos0=0))
+    assert L.indexcache_forward_c(b"F", 1, arr, 16, None, None, 0, None) == 3
+
+
+def test_binding_rejects_non_dense_layouts():
+    """The kernels read q, w, idx and out densely and k/kv rows back to back;
+    the binding refuses views with other strides instead of passing a base
+    pointer that would be read with the wrong layout."""
+    import torch
+    q = torch.zeros(1, 8, 4, 32)
+    k = torch.zeros(1, 8, 32)
+    w = torch.zeros(1, 8, 4)
+    L.indexer_args(q, k, w)                                           # dense: fine
+    L.indexer_args(q, torch.zeros(2, 20, 32)[:, :8], torch.zeros(2, 8, 4).contiguous()[:1])  # batch stride: fine
+    with pytest.raises(ValueError):
+        L.indexer_args(q.transpose(1, 2).contiguous().transpose(1, 2), k, w)   # head/row transposed q
+    with pytest.raises(ValueError):
+        L.indexer_args(q, torch.zeros(1, 8, 64)[..., :32], w)                  # k rows with stride 64
+    with pytest.raises(ValueError):
+        L.indexer_args(q, k, torch.zeros(1, 4, 8).transpose(1, 2))             # transposed w
+    Q = torch.zeros(1, 4, 16, 576)
+    kv = torch.zeros(1, 10, 1, 576)
+    idx = torch.zeros(1, 4, 16, dtype=torch.int32)
+    out = torch.zeros(1, 4, 16, 512)
+    L.sparse_attn_args(Q, kv, idx, 1.0, out)                          # dense: fine
+    L.sparse_attn_args(Q, torch.zeros(2, 30, 1, 576)[:, :10], idx, 1.0, out)   # batch stride: fine
+    with pytest.raises(ValueError):
+        L.sparse_attn_args(torch.zeros(1, 4, 32, 576)[:, :, :16], kv, idx, 1.0, out)   # head slice of Q
+    with pytest.raises(ValueError):
+        L.sparse_attn_args(Q, torch.zeros(1, 10, 1, 640)[..., :576], idx, 1.0, out)    # strided kv rows
+    with pytest.raises(ValueError):
+        L.sparse_attn_args(Q, kv, torch.zeros(1, 16, 4, dtype=torch.int32).transpose(1, 2), 1.0, out)
+    with pytest.raises(ValueError):
+        L.sparse_attn_args(Q, kv, idx, 1.0, torch.zeros(1, 4, 16, 1024)[..., :512])
