@@ -56,17 +56,23 @@ def parse():
                    help="similarity-based pattern search instead of the bench line: the similarity matrix "
                         "of a 47-layer calibration prefill (L=--similarity-len, drifting indexer keys) and "
                         "the dynamic-program patterns at 24/12/7 F layers; prints one JSON object")
+    p.add_argument("--mli", action="store_true",
+                   help="multi-layer-indexer shift instead of the bench line: the prefill stack (FSSSFSSS) and "
+                        "the decode stack (FSSS) under plain IndexCache and under the shifted loop (indexers on a "
+                        "second stream beside attention, and on one stream), same inputs; prints one JSON object")
     p.add_argument("--similarity-len", type=int, default=16384)
     p.add_argument("--similarity-layers", type=int, default=47)
     p.add_argument("--layer", choices=["prefill_bf16_L16384", "prefill_fp8_L65536"], default=None,
                    help="one prefill F layer of a named workload instead of the bench line: the fused "
                         "indexer+Top-k (and, for the fp8 layer, its 16-head MLA sparse attention) timed with HIP "
                         "events over --kernel-reps launches; prints one JSON object")
-    p.add_argument("--profile", choices=["indexer", "attn", "copy"], default=None,
+    p.add_argument("--profile", choices=["indexer", "attn", "copy", "gather"], default=None,
                    help="counter-collection runs: 'indexer' launches only the prefill F layer's fused "
                         "indexer+Top-k (3 launches, the first a warm-up); 'attn' that layer's prefill "
                         "sparse attention (3 launches after one indexer launch); 'copy' runs a 1 GiB read + "
-                        "1 GiB write elementwise kernel, the calibration for the HBM byte counters")
+                        "1 GiB write elementwise kernel, the calibration for the HBM byte counters; 'gather' "
+                        "times the prefill attention of that layer and the gather probe's access patterns over the "
+                        "same index tensor and latent rows, and prints one JSON object")
     return p.parse_args()
 
 
@@ -152,8 +158,57 @@ def cpu_baseline(ix, topk, seconds):
             break
     dt = time.perf_counter() - t0
     return {"value": pairs / dt, "unit": "score-pairs/s", "cores": int(threads), "kind": "oracle",
+            "host_cpu_count": os.cpu_count(), "blas_threads": int(threads),
             "sample": f"{rows} random query rows of the L={L} bf16 F layer (indexer + Top-k k={topk}), "
-                      f"{pairs} causal pairs in {dt:.1f} s, float64 NumPy"}
+                      f"{pairs} causal pairs in {dt:.1f} s, float64 NumPy; `cores` = the BLAS threads the "
+                      f"oracle ran on ({os.cpu_count()} logical CPUs on the host)"}
+
+
+PROBE_MODES = {0: "quarter rows, 2 steps in flight (the attention kernel's pattern)",
+               1: "whole rows per wave, 64 B of 16 rows per load, 2 steps",
+               2: "whole rows per wave, rows end to end, 2 steps",
+               3: "quarter rows, 4 steps in flight",
+               4: "whole rows per wave, 64 B of 16 rows per load, 3 steps",
+               5: "whole rows per wave, rows end to end, 3 steps"}
+
+
+def gather_ceiling(dsa, kv, idx, reps):
+    """Rate at which the chip gathers the selected 1152-byte latent rows of idx
+    from kv with no arithmetic (the gather probe, every access pattern it has);
+    returns {mode: (ms per launch, gathered GB/s)}."""
+    n_sel = int((idx >= 0).sum().item())
+    out = {}
+    for mode in PROBE_MODES:
+        dsa.gather_probe(kv, idx, mode)
+        torch.cuda.synchronize()
+        ms = time_batch(lambda: dsa.gather_probe(kv, idx, mode), reps)
+        out[mode] = (ms, n_sel * 1152 / (ms * 1e-3) / 1e9)
+    return out
+
+
+def sa_roofline(sa_ms, n_sel, probe):
+    """Prefill sparse attention against its two bounds: the gather rate of the
+    selected latent rows (against the probe's best pattern on the same index
+    tensor, and against HBM peak for scale) and the bf16 MFMA rate of its
+    2 x 16 x (576 + 512) flop per (query, selected position)."""
+    gathered = n_sel * 1152
+    flop = n_sel * 2 * 16 * (576 + 512)
+    gbs = gathered / (sa_ms * 1e-3) / 1e9
+    best_mode = max(probe, key=lambda m: probe[m][1])
+    ceiling = probe[best_mode][1]
+    tflops = flop / (sa_ms * 1e-3) / 1e12
+    return {
+        "kernel": "sa_mla4_kernel (prefill sparse attention, bf16 MLA 16 heads 576/512)",
+        "bound": "gather", "achieved": gbs, "peak": ceiling, "unit": "GB/s", "frac": gbs / ceiling,
+        "peak_source": f"gather probe, best pattern: mode {best_mode} ({PROBE_MODES[best_mode]}), measured live "
+                       "on the same index tensor and latent rows",
+        "hbm_peak_frac": gbs / PEAK_HBM_GBS,
+        "mfma_achieved_TFLOPs": tflops, "mfma_peak_TFLOPs": PEAK_BF16_TFLOPS, "mfma_frac": tflops / PEAK_BF16_TFLOPS,
+        "algorithmic_per_launch": f"{n_sel} (query, selected position) pairs x 1152 B = {gathered:.4g} B; "
+                                  f"x 34816 flop = {flop:.4g} flop",
+        "launch_ms": sa_ms,
+        "probe_GBs": {str(m): round(v[1], 1) for m, v in probe.items()},
+    }
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_indexer_topk_bf16_L131072_traffic.md")
@@ -202,6 +257,22 @@ def profile_run(args, dev):
     import dsa_lightning_indexer_amd as dsa
     from synth import inputs as syn
     L = args.prefill_len
+    if args.profile == "gather":
+        ix, sa = syn.prefill_stack_layers(L=L, n_layers=1, seed=4, device=dev)[0]
+        idx = dsa.topk(ix.q, ix.k, ix.w, 2048)
+        out = torch.empty((1, L, 16, 512), dtype=torch.float32, device=dev)
+        dsa.sparse_attn(sa.q, sa.kv, idx, sa.scale, d_v=512, out=out)
+        torch.cuda.synchronize()
+        reps = max(args.kernel_reps, 3)
+        sa_ms = time_batch(lambda: dsa.sparse_attn(sa.q, sa.kv, idx, sa.scale, d_v=512, out=out), reps)
+        kv = sa.kv[0, :, 0]
+        probe = gather_ceiling(dsa, kv, idx[0], reps)
+        for m, (ms, gbs) in probe.items():
+            print(f"profile gather: mode {m} ({PROBE_MODES[m]}): {ms:.3f} ms, {gbs:.1f} GB/s", flush=True)
+        n_sel = int((idx >= 0).sum().item())
+        print(json.dumps({"workload": f"prefill layer L={L}, k=2048, latent rows 1152 B",
+                          "roofline_sa": sa_roofline(sa_ms, n_sel, probe)}), flush=True)
+        return
     if args.profile == "attn":
         # the step's first prefill layer: its sparse attention over its F layer's index tensor
         ix, sa = syn.prefill_stack_layers(L=L, n_layers=1, seed=4, device=dev)[0]
@@ -424,6 +495,63 @@ def similarity_run(args, dev):
     print(json.dumps(rec), flush=True)
 
 
+def mli_run(args, dev):
+    """Plain IndexCache against the multi-layer-indexer shift at equal retention
+    (same kernels, same inputs): stack time with HIP events on the attention
+    stream, which the shifted loop joins with its indexer stream at the end."""
+    import dsa_lightning_indexer_amd as dsa
+    from synth import inputs as syn
+    topk = 2048
+    side = torch.cuda.Stream(device=dev)
+    res = {"metric": "stack time, plain IndexCache vs the multi-layer-indexer shift", "unit": "ms",
+           "data": "synthetic"}
+
+    def measure(pattern, specs, reps):
+        ws = torch.empty(max(dsa.indexcache_forward_workspace_size(pattern, specs, topk), 256),
+                         dtype=torch.uint8, device=dev)
+        ws2 = torch.empty(max(dsa.indexcache_forward_mli_workspace_size(pattern, specs, topk), 256),
+                          dtype=torch.uint8, device=dev)
+        runs = {"indexcache": lambda: dsa.indexcache_forward(pattern, specs, topk, ws=ws),
+                "mli_two_streams": lambda: dsa.indexcache_forward_mli(pattern, specs, topk, index_stream=side,
+                                                                      ws=ws2),
+                "mli_one_stream": lambda: dsa.indexcache_forward_mli(pattern, specs, topk, ws=ws2)}
+        for f in runs.values():
+            f()
+        torch.cuda.synchronize()
+        out = {}
+        # interleaved repetitions so that clock drift hits every variant alike
+        times = {k: [] for k in runs}
+        for _ in range(reps):
+            for k, f in runs.items():
+                times[k].append(time_launches(f, 1)[0])
+        for k, t in times.items():
+            t = sorted(t)
+            out[k] = {"median_ms": t[len(t) // 2], "min_ms": t[0]}
+        base = out["indexcache"]["median_ms"]
+        for k in out:
+            out[k]["speedup_vs_indexcache"] = base / out[k]["median_ms"]
+        return out
+
+    B, S, NL = args.decode_batch, args.decode_len, args.decode_layers
+    pattern_d, dspecs = decode_stack(dsa, syn, B, S, NL, topk, dev)
+    torch.cuda.synchronize()
+    r = measure(pattern_d, dspecs, 9)
+    log(f"mli decode: " + ", ".join(f"{k} {v['median_ms']:.3f} ms" for k, v in r.items()))
+    res["decode"] = {"workload": f"decode stack B={B} x S={S} x {NL} layers {pattern_d.count('F')} F (FSSS), fp8 "
+                                 f"indexer K cache, k={topk}", "pattern": pattern_d, "results": r}
+    del dspecs
+    torch.cuda.empty_cache()
+    L = args.prefill_len
+    pattern_p = "FSSSFSSS"
+    _, pspecs = prefill_stack(dsa, syn, L, pattern_p, topk, dev)
+    torch.cuda.synchronize()
+    r = measure(pattern_p, pspecs, 3)
+    log(f"mli prefill: " + ", ".join(f"{k} {v['median_ms']:.1f} ms" for k, v in r.items()))
+    res["prefill"] = {"workload": f"prefill stack L={L} x 8 layers {pattern_p}, bf16 indexer, k={topk}",
+                      "pattern": pattern_p, "results": r}
+    print(json.dumps(res), flush=True)
+
+
 def sweep_run(args, dev):
     """Stack time per sharing pattern (same kernels and driver as the bench line)."""
     import dsa_lightning_indexer_amd as dsa
@@ -524,6 +652,9 @@ def main():
     if args.sweep:
         sweep_run(args, dev)
         return
+    if args.mli:
+        mli_run(args, dev)
+        return
     if args.distill:
         distill_run(args, dev)
         return
@@ -605,6 +736,17 @@ def main():
     d_ms = sum(dtimes) / len(dtimes)
     scan_bytes = B * S * (128 + 4)
 
+    # prefill sparse attention (layer 1 over layer 0's index tensor) and its gather ceiling
+    sa1 = pspecs[1]["sa"]
+    idx0 = pspecs[0]["idx_out"]
+    sa_ms = sum(time_launches(lambda: dsa.sparse_attn(sa1["q"], sa1["kv"], idx0, sa1["scale"], d_v=512,
+                                                      out=sa1["out"]), args.kernel_reps)) / args.kernel_reps
+    n_sel = int((idx0 >= 0).sum().item())
+    probe = gather_ceiling(dsa, sa1["kv"][0, :, 0], idx0[0], max(args.kernel_reps, 3))
+    roof_sa = sa_roofline(sa_ms, n_sel, probe)
+    log(f"prefill sparse attention: {sa_ms:.2f} ms/launch, {roof_sa['achieved']:.0f} GB/s gathered "
+        f"({roof_sa['frac']:.3f} of the probe's {roof_sa['peak']:.0f} GB/s), MFMA {roof_sa['mfma_frac']:.3f}")
+
     n_f_p = pattern_p.count("F")
     n_f_d = pattern_d.count("F")
     pairs_step = n_f_p * pairs_layer + n_f_d * B * S
@@ -653,6 +795,7 @@ def main():
             "algorithmic_per_launch": f"{pairs_layer} causal pairs x 16384 flop = {flop_layer:.4g} flop",
             "launch_ms": k_ms,
         },
+        "roofline_sa": roof_sa,
     }
 
     if not args.no_report:
@@ -666,9 +809,6 @@ def main():
         ws_f = torch.empty(max(dsa.indexcache_forward_workspace_size(pattern_f, fspecs, topk), 256),
                            dtype=torch.uint8, device=dev)
         ms_allf = time_launches(lambda: dsa.indexcache_forward(pattern_f, fspecs, topk, ws=ws_f), 1)[0]
-        sa0 = pspecs[1]["sa"]
-        sa_ms = sum(time_launches(lambda: dsa.sparse_attn(sa0["q"], sa0["kv"], pspecs[0]["idx_out"],
-                                                          sa0["scale"], d_v=512, out=sa0["out"]), 2)) / 2
         rows = L - topk + 1
         M = [[1.0] * len(pattern_f) for _ in pattern_f]
         for i in range(len(pattern_f)):

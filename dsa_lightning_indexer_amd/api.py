@@ -107,6 +107,32 @@ def indexcache_forward(pattern, specs, k, *, ws=None):
     return list(src)
 
 
+def indexcache_forward_mli_workspace_size(pattern, specs, k):
+    arr = _layers(specs, k)
+    return L.indexcache_forward_mli_workspace_size(pattern.encode(), len(specs), arr, k)
+
+
+def indexcache_forward_mli(pattern, specs, k, *, index_stream=None, ws=None):
+    """IndexCache loop with the multi-layer-indexer shift: layer l attends with
+    the nearest earlier F layer's index tensor (layer 0 with its own); F-layer
+    indexers run on `index_stream` (a torch.cuda.Stream; None = the current
+    stream, i.e. in order), attention on the current stream.  Same specs as
+    indexcache_forward; returns the 0-based source layer of every layer."""
+    arr = _layers(specs, k)
+    n = len(specs)
+    need = L.indexcache_forward_mli_workspace_size(pattern.encode(), n, arr, k)
+    dev = specs[0]["sa"]["q"].device
+    wbuf, wbytes = _ws(need, dev, ws)
+    src = (ctypes.c_int32 * n)()
+    main = _stream()
+    side = main if index_stream is None else ctypes.c_void_p(index_stream.cuda_stream)
+    L.check(L.indexcache_forward_mli_c(pattern.encode(), n, arr, k, src,
+                                       None if wbuf is None else wbuf.data_ptr(), wbytes, main, side))
+    if index_stream is not None and ws is None and wbuf is not None:
+        wbuf.record_stream(index_stream)
+    return list(src)
+
+
 def index_overlap(a, b, k, *, rows=None, row_counts=None, total=None):
     """Adds sum_r |a[r] ∩ b[r]| to `total` (uint64 stored in an int64 tensor of one element);
     optionally writes per-row counts.  a, b: int32 [rows, k] (any leading dims flattened)."""
@@ -218,3 +244,19 @@ def pattern_search(S, n_full):
     L.check(L.dsa_pattern_search(S.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), n, int(n_full), buf,
                                  ctypes.byref(score)))
     return buf.value.decode(), score.value
+
+
+def gather_probe(kv, idx, mode, *, out=None):
+    """Measurement helper: read every selected 1152-byte latent row (kv
+    [n_rows, 576] bf16 or [n_rows, 1, 576]) of idx [n_q, topk] with access
+    pattern `mode` (0..5); returns the uint32 checksums (as int32)."""
+    n_rows = kv.shape[0]
+    L._dense("kv", kv)
+    L._dense("idx", idx)
+    idx2 = idx.reshape(-1, idx.shape[-1])
+    n_q, topk = idx2.shape
+    words = L.dsa_gather_probe_out_words(n_q, mode)
+    if out is None:
+        out = torch.empty(max(words, 1), dtype=torch.int32, device=kv.device)
+    L.check(L.dsa_gather_probe(kv.data_ptr(), n_rows, idx2.data_ptr(), n_q, topk, mode, out.data_ptr(), _stream()))
+    return out

@@ -217,6 +217,11 @@ dsa_status check_sa(const dsa_sparse_attn_args* a, bool need_idx, bool need_out 
 
 }  // namespace
 
+namespace dsa_host {
+// Error text for callers in other translation units (same thread-local buffer).
+dsa_status set_error(dsa_status st, const char* msg) { return fail(st, "%s", msg); }
+}  // namespace dsa_host
+
 extern "C" {
 
 int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
@@ -281,8 +286,10 @@ dsa_status dsa_sparse_attn(const dsa_sparse_attn_args* a, void* ws, size_t ws_by
   return hip_status(dsa_host::sparse_attn_launch(*a, ws, stream), "sparse attention launch");
 }
 
+// ws_topk / ws_attn (optional): the largest Top-k and attention workspace needs
+// on their own (the overlapped loop gives each its own region).
 static dsa_status check_forward(const char* pattern, int32_t n, const dsa_layer* layers, int32_t k,
-                                size_t* ws_need) {
+                                size_t* ws_need, size_t* ws_topk = nullptr, size_t* ws_attn = nullptr) {
   if (!pattern) return fail(DSA_ERR_INVALID, "pattern is NULL");
   if (n < 1) return fail(DSA_ERR_INVALID, "n_layers must be >= 1");
   if ((int64_t)strnlen(pattern, (size_t)n + 1) != n)
@@ -293,7 +300,7 @@ static dsa_status check_forward(const char* pattern, int32_t n, const dsa_layer*
   if (pattern[0] != 'F') return fail(DSA_ERR_INVALID, "the first layer must be F");
   if (!layers) return fail(DSA_ERR_INVALID, "layers is NULL");
   if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID, "k must be 1..%d", DSA_MAX_TOPK);
-  size_t need = 0;
+  size_t need = 0, need_topk = 0, need_attn = 0;
   int32_t src = -1;
   for (int32_t l = 0; l < n; ++l) {
     const dsa_layer& L = layers[l];
@@ -305,7 +312,7 @@ static dsa_status check_forward(const char* pattern, int32_t n, const dsa_layer*
       if (st != DSA_OK) return fail(st, "layer %d (F): %s", l, g_last_error.c_str());
       if (!L.idx_out || !aligned(L.idx_out, 4)) return fail(DSA_ERR_INVALID, "layer %d (F): idx_out NULL/misaligned", l);
       const size_t w = topk_ws(&L.ix, nullptr);
-      if (w > need) need = w;
+      if (w > need_topk) need_topk = w;
     }
     dsa_status st = check_sa(&L.sa, false);
     if (st != DSA_OK) return fail(st, "layer %d: %s", l, g_last_error.c_str());
@@ -314,11 +321,55 @@ static dsa_status check_forward(const char* pattern, int32_t n, const dsa_layer*
       return fail(DSA_ERR_INVALID, "layer %d: attention batch/n_q/topk (%d,%d,%d) must match the cached "
                   "index tensor (%d,%d,%d)", l, L.sa.batch, L.sa.n_q, L.sa.topk, S.batch, S.n_q, k);
     const size_t w = align_up(dsa_host::sparse_attn_ws_bytes(L.sa));
-    if (w > need) need = w;
+    if (w > need_attn) need_attn = w;
   }
+  need = need_topk > need_attn ? need_topk : need_attn;
   *ws_need = need;
+  if (ws_topk) *ws_topk = need_topk;
+  if (ws_attn) *ws_attn = need_attn;
   return DSA_OK;
 }
+
+// The overlapped loop's extra conditions: an F layer l > first attends with the
+// previous F layer's tensor while its own indexer writes idx_out, so the
+// shapes must agree and the two buffers must differ.
+static dsa_status check_forward_mli(const char* pattern, int32_t n, const dsa_layer* layers, int32_t k,
+                                    size_t* ws_need, size_t* ws_topk) {
+  size_t need = 0, need_topk = 0, need_attn = 0;
+  dsa_status st = check_forward(pattern, n, layers, k, &need, &need_topk, &need_attn);
+  if (st != DSA_OK) return st;
+  int32_t prev = -1;
+  for (int32_t l = 0; l < n; ++l) {
+    if (pattern[l] != 'F') continue;
+    if (prev >= 0) {
+      const dsa_layer& L = layers[l];
+      const dsa_indexer_args& P = layers[prev].ix;
+      if (L.sa.batch != P.batch || L.sa.n_q != P.n_q)
+        return fail(DSA_ERR_INVALID, "layer %d: attention batch/n_q (%d,%d) must match the index tensor of F "
+                    "layer %d (%d,%d) it attends with", l, L.sa.batch, L.sa.n_q, prev, P.batch, P.n_q);
+      if (L.idx_out == layers[prev].idx_out)
+        return fail(DSA_ERR_INVALID, "layers %d and %d (consecutive F layers) share idx_out: the overlapped loop "
+                    "writes one while attention reads the other", prev, l);
+    }
+    prev = l;
+  }
+  // the indexer stream and the attention stream each get their own region
+  *ws_topk = need_topk;
+  *ws_need = need_topk + need_attn;
+  return DSA_OK;
+}
+
+}  // extern "C"
+
+namespace dsa_host {
+dsa_status forward_workspace_need(const char* pattern, int32_t n, const dsa_layer* layers, int32_t k, size_t* need) {
+  g_last_error.clear();
+  *need = 0;
+  return check_forward(pattern, n, layers, k, need);
+}
+}  // namespace dsa_host
+
+extern "C" {
 
 size_t indexcache_forward_workspace_size(const char* pattern, int32_t n, const dsa_layer* layers, int32_t k) {
   size_t need = 0;
@@ -354,6 +405,92 @@ dsa_status indexcache_forward(const char* pattern, int32_t n, const dsa_layer* l
     if (st != DSA_OK) return st;
   }
   return DSA_OK;
+}
+
+size_t indexcache_forward_mli_workspace_size(const char* pattern, int32_t n, const dsa_layer* layers, int32_t k) {
+  size_t need = 0, need_topk = 0;
+  if (check_forward_mli(pattern, n, layers, k, &need, &need_topk) != DSA_OK) return 0;
+  return need;
+}
+
+dsa_status indexcache_forward_mli(const char* pattern, int32_t n, const dsa_layer* layers, int32_t k,
+                                  int32_t* src_layer, void* ws, size_t ws_bytes, hipStream_t stream,
+                                  hipStream_t index_stream) {
+  g_last_error.clear();
+  size_t need = 0, need_topk = 0;
+  dsa_status st = check_forward_mli(pattern, n, layers, k, &need, &need_topk);
+  if (st != DSA_OK) return st;
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
+  if (ws && !aligned(ws, kAlign)) return fail(DSA_ERR_INVALID, "workspace must be 256-byte aligned");
+  void* ws_index = ws;
+  void* ws_attn = need > need_topk ? (void*)((uint8_t*)ws + need_topk) : nullptr;
+  const bool two = index_stream != stream;
+  // One event per F layer marks its index tensor done (on the indexer stream);
+  // one marks where the attention stream stands when layer l starts (the
+  // layer's input is ready): layer l's indexer waits for it.
+  int32_t n_f = 0;
+  for (int32_t l = 0; l < n; ++l) n_f += pattern[l] == 'F';
+  hipEvent_t* ev = nullptr;
+  int32_t n_ev = 0;
+  auto cleanup = [&]() {
+    for (int32_t i = 0; i < n_ev; ++i) (void)hipEventDestroy(ev[i]);
+    delete[] ev;
+  };
+  if (two) {
+    ev = new hipEvent_t[2 * (size_t)n_f];
+    for (; n_ev < 2 * n_f; ++n_ev) {
+      hipError_t e = hipEventCreateWithFlags(&ev[n_ev], hipEventDisableTiming);
+      if (e != hipSuccess) {
+        cleanup();
+        return hip_status(e, "event create");
+      }
+    }
+  }
+  int32_t prev = -1;        // latest F layer whose indexer was enqueued
+  int32_t fi = 0;           // F layers seen so far
+  int32_t waited = -1;      // latest F layer the attention stream has waited for
+  hipError_t e = hipSuccess;
+  for (int32_t l = 0; l < n && e == hipSuccess && st == DSA_OK; ++l) {
+    const dsa_layer& L = layers[l];
+    int32_t done_ev = -1;
+    if (pattern[l] == 'F') {
+      if (two) {
+        e = hipEventRecord(ev[2 * fi], stream);                       // layer l's input is ready
+        if (e == hipSuccess) e = hipStreamWaitEvent(index_stream, ev[2 * fi], 0);
+        if (e != hipSuccess) break;
+      }
+      st = run_topk(&L.ix, nullptr, k, L.idx_out, ws_index, two ? index_stream : stream);
+      if (st != DSA_OK) break;
+      if (two) e = hipEventRecord(ev[2 * fi + 1], index_stream);
+      done_ev = 2 * fi + 1;
+      ++fi;
+    }
+    // attend with the previous F layer's tensor; the first layer with its own
+    const int32_t src = prev >= 0 ? prev : l;
+    if (src_layer) src_layer[l] = src;
+    if (two && src > waited && e == hipSuccess) {
+      // the event of F layer src: its own (first layer) or the one recorded when it ran
+      int32_t src_ev = done_ev;
+      if (src != l) {
+        int32_t f = 0;
+        for (int32_t j = 0; j < src; ++j) f += pattern[j] == 'F';
+        src_ev = 2 * f + 1;
+      }
+      e = hipStreamWaitEvent(stream, ev[src_ev], 0);
+      waited = src;
+    }
+    if (e != hipSuccess) break;
+    dsa_sparse_attn_args sa = L.sa;
+    sa.idx = layers[src].idx_out;
+    st = hip_status(dsa_host::sparse_attn_launch(sa, ws_attn, stream), "sparse attention launch");
+    if (pattern[l] == 'F') prev = l;
+  }
+  // join: later work on `stream` is ordered after every indexer of this call
+  if (two && e == hipSuccess && st == DSA_OK && fi > 0) e = hipStreamWaitEvent(stream, ev[2 * (fi - 1) + 1], 0);
+  cleanup();
+  if (st != DSA_OK) return st;
+  return hip_status(e, "stream ordering");
 }
 
 dsa_status dsa_indexer_distill(const dsa_distill_args* a, hipStream_t stream) {
@@ -489,6 +626,26 @@ dsa_status dsa_similarity_matrix(int32_t n, const dsa_layer* layers, int32_t k, 
     }
   }
   return DSA_OK;
+}
+
+int64_t dsa_gather_probe_out_words(int64_t n_q, int32_t mode) {
+  if (n_q < 1 || mode < 0 || mode > 5) return 0;
+  return dsa_host::gather_probe_out_words(n_q, mode);
+}
+
+dsa_status dsa_gather_probe(const void* table, int32_t n_rows, const int32_t* idx, int64_t n_q, int32_t topk,
+                            int32_t mode, uint32_t* out, hipStream_t stream) {
+  g_last_error.clear();
+  if (mode < 0 || mode > 5) return fail(DSA_ERR_INVALID, "mode must be 0..5");
+  if (n_rows < 1 || (int64_t)n_rows * 1152 >= ((int64_t)1 << 31))
+    return fail(DSA_ERR_UNSUPPORTED, "n_rows must be 1..%lld (1152-byte rows, 32-bit offsets)",
+                (long long)((((int64_t)1 << 31) - 1) / 1152));
+  if (n_q < 1 || n_q > (int64_t)INT32_MAX) return fail(DSA_ERR_INVALID, "n_q must be 1..2^31 - 1");
+  if (topk < 1 || topk > DSA_MAX_TOPK) return fail(DSA_ERR_INVALID, "topk must be 1..%d", DSA_MAX_TOPK);
+  if (!table || !idx || !out) return fail(DSA_ERR_INVALID, "table, idx and out are required");
+  if (!aligned(table, 16) || !aligned(idx, 4) || !aligned(out, 4))
+    return fail(DSA_ERR_INVALID, "table must be 16-byte aligned, idx and out 4-byte aligned");
+  return hip_status(dsa_host::gather_probe_launch(table, n_rows, idx, n_q, topk, mode, out, stream), "probe launch");
 }
 
 dsa_status dsa_pattern_search(const double* S, int32_t n, int32_t n_full, char* pattern, double* score) {

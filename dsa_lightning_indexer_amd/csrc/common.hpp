@@ -147,6 +147,16 @@ hipError_t overlap_launch(const int32_t* a, const int32_t* b, int64_t rows, int3
 hipError_t row_cosine_launch(const float* a, const float* b, int64_t rows, int64_t width, float* row_cos,
                              double* mean, hipStream_t s);
 hipError_t identity_f64_launch(double* m, int64_t n, hipStream_t s);
+// Gather-bandwidth probe over 1152-byte latent rows (gather_probe.hip).
+int64_t gather_probe_out_words(int64_t n_q, int32_t mode);
+hipError_t gather_probe_launch(const void* table, int32_t n_rows, const int32_t* idx, int64_t n_q, int32_t topk,
+                               int32_t mode, uint32_t* out, hipStream_t s);
+
+// indexcache_forward's validation and workspace need (api.cpp).
+dsa_status forward_workspace_need(const char* pattern, int32_t n, const dsa_layer* layers, int32_t k, size_t* need);
+// Sets the thread-local text dsa_last_error() returns (api.cpp) and returns st.
+dsa_status set_error(dsa_status st, const char* msg);
+
 // Sharing-pattern dynamic program, host code (pattern_search.cpp).  False if no
 // admissible pattern exists.
 bool pattern_search_dp(const double* S, int n, int M, char* pattern, double* score);

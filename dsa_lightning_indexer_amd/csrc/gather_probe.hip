@@ -1,0 +1,158 @@
+// Gather-bandwidth probe (a measurement helper, not a step of the method): reads
+// the selected 1152-byte latent rows of every query's index row, as a sparse
+// attention pass must ([DSA-NOTES] §3: each query reads the k rows its index
+// set names), with no arithmetic beyond an XOR checksum that keeps every load
+// alive.  Its rate is the ceiling the sparse-attention kernel's gathers are
+// measured against.  Access patterns (16 selected positions per step, DEPTH
+// steps in flight, positions staged in LDS, invalid entries read as zeros):
+//   mode 0  quarter rows: one query per four-wave workgroup; wave w reads the
+//           bytes the attention kernel's wave w reads (V columns 128w..128w+127
+//           and, for w < 2, rope columns 512 + 32w..), 64 bytes of 16 rows per
+//           load instruction
+//   mode 1  whole rows, strided: one query per wave (four per workgroup); each
+//           load instruction covers 64 bytes of each of 16 rows
+//   mode 2  whole rows, contiguous: one query per wave; load j of a step covers
+//           the j-th KiB of the step's 16 rows laid end to end (eight lanes per
+//           128-byte line)
+// mode + 3: the same pattern with deeper prefetch: four steps in flight for
+//           quarter rows, three for whole rows (four would not fit the
+//           register file).
+#include "common.hpp"
+
+namespace {
+
+using namespace dsa;
+
+constexpr int kRowB = 1152;            // 576 bf16 latent columns
+constexpr int kChunks = kRowB / 16;    // 16-byte chunks per row
+constexpr int kStep = 16;              // positions per step
+constexpr int kMaxK = DSA_MAX_TOPK;
+
+struct ProbeParams {
+  const void* table;
+  uint32_t table_bytes;
+  const int32_t* idx;
+  int64_t n_q;
+  int32_t n_rows, topk;
+  uint32_t* out;
+};
+
+__device__ __forceinline__ uint32_t xor4(u32x4 v) { return v[0] ^ v[1] ^ v[2] ^ v[3]; }
+
+template <int MODE>
+struct Pattern;
+
+// quarter rows: lane (g, col) reads chunks of row `col` of the step
+template <>
+struct Pattern<0> {
+  static constexpr int kLoads = 5;
+  static constexpr int kQueriesPerWg = 1;
+  __device__ static uint32_t offset(int w, int lane, int j, uint32_t rowbase) {
+    const int g = lane >> 4;
+    if (j < 4) return rowbase + 256 * w + 64 * j + 16 * g;
+    return w < 2 ? rowbase + 1024 + 64 * w + 16 * g : 0x80000000u;
+  }
+  __device__ static int row_of(int lane, int) { return lane & 15; }
+};
+
+// whole rows, 64 bytes of 16 rows per instruction
+template <>
+struct Pattern<1> {
+  static constexpr int kLoads = kChunks / 4;     // 18
+  static constexpr int kQueriesPerWg = 4;
+  __device__ static uint32_t offset(int, int lane, int j, uint32_t rowbase) {
+    return rowbase + 64 * j + 16 * (lane >> 4);
+  }
+  __device__ static int row_of(int lane, int) { return lane & 15; }
+};
+
+// whole rows end to end: chunk c = 64 j + lane of the step's 16 x 72 chunks
+template <>
+struct Pattern<2> {
+  static constexpr int kLoads = kStep * kChunks / 64;   // 18
+  static constexpr int kQueriesPerWg = 4;
+  __device__ static uint32_t offset(int, int lane, int j, uint32_t rowbase) {
+    return rowbase + 16 * ((64 * j + lane) % kChunks);
+  }
+  __device__ static int row_of(int lane, int j) { return (64 * j + lane) / kChunks; }
+};
+
+template <int MODE, int DEPTH>
+__global__ __launch_bounds__(256) void gather_probe_kernel(ProbeParams p) {
+  using P = Pattern<MODE>;
+  constexpr int QW = P::kQueriesPerWg;
+  __shared__ int32_t sidx[QW][kMaxK];
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id();
+  const int64_t q0 = (int64_t)blockIdx.x * QW;
+  for (int qq = 0; qq < QW; ++qq) {
+    const int64_t q = q0 + qq;
+    for (int e = threadIdx.x; e < p.topk; e += 256) sidx[qq][e] = q < p.n_q ? p.idx[q * p.topk + e] : -1;
+  }
+  __syncthreads();
+  const int qq = QW == 1 ? 0 : w;
+  const int64_t q = q0 + qq;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.table), (short)0, (int)p.table_bytes, 0x00020000);
+  const int nsteps = (p.topk + kStep - 1) / kStep;
+
+  auto issue = [&](int step, u32x4 (&buf)[P::kLoads]) {
+#pragma unroll
+    for (int j = 0; j < P::kLoads; ++j) {
+      const int e = step * kStep + P::row_of(lane, j);
+      const int32_t s = (step < nsteps && e < p.topk) ? sidx[qq][e] : -1;
+      const bool valid = s >= 0 && s < p.n_rows;
+      const uint32_t base = valid ? (uint32_t)s * kRowB : 0x80000000u;
+      const uint32_t off = P::offset(w, lane, j, base);
+      buf[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    }
+  };
+  u32x4 buf[DEPTH][P::kLoads];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) issue(d, buf[d]);
+  uint32_t acc = 0;
+  for (int step = 0; step < nsteps; step += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+#pragma unroll
+      for (int j = 0; j < P::kLoads; ++j) acc ^= xor4(buf[d][j]);
+      issue(step + DEPTH + d, buf[d]);
+    }
+  }
+  // fold the wave's checksum into lane 0 and store one word per wave
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o, 64);
+  if (lane == 0 && q < p.n_q) p.out[(int64_t)blockIdx.x * 4 + w] = acc;
+}
+
+template <int MODE, int DEPTH>
+void launch(const ProbeParams& p, hipStream_t s) {
+  const int64_t wgs = (p.n_q + Pattern<MODE>::kQueriesPerWg - 1) / Pattern<MODE>::kQueriesPerWg;
+  hipLaunchKernelGGL((gather_probe_kernel<MODE, DEPTH>), dim3((unsigned)wgs), dim3(256), 0, s, p);
+}
+
+}  // namespace
+
+namespace dsa_host {
+
+int64_t gather_probe_out_words(int64_t n_q, int32_t mode) {
+  const int qw = (mode % 3) == 0 ? 1 : 4;
+  return (n_q + qw - 1) / qw * 4;
+}
+
+hipError_t gather_probe_launch(const void* table, int32_t n_rows, const int32_t* idx, int64_t n_q, int32_t topk,
+                               int32_t mode, uint32_t* out, hipStream_t s) {
+  ProbeParams p{table, (uint32_t)((int64_t)n_rows * kRowB), idx, n_q, n_rows, topk, out};
+  switch (mode) {
+    case 0: launch<0, 2>(p, s); break;
+    case 1: launch<1, 2>(p, s); break;
+    case 2: launch<2, 2>(p, s); break;
+    case 3: launch<0, 4>(p, s); break;
+    case 4: launch<1, 3>(p, s); break;
+    case 5: launch<2, 3>(p, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsa_host

@@ -180,6 +180,34 @@ dsa_status indexcache_forward(const char* pattern, int32_t n_layers, const dsa_l
                               hipStream_t stream);
 
 /*
+ * IndexCache loop with the multi-layer-indexer shift ([MLI] "核心思路" and
+ * "与 IndexCache／IndexShare 的组合"; [MLI] is the page "MLI重构DeepSeek稀疏注意力：
+ * 跨层复用索引免训提速", zicq.com): layer l attends with the index tensor of the
+ * nearest F layer before it (layer 0 with its own), so an F layer's indexer no
+ * longer precedes its own attention and can run beside it.
+ *   Same pattern, layers, k and src_layer as indexcache_forward; src_layer[l]
+ *   receives the shifted source.  Consecutive F layers need distinct idx_out
+ *   buffers (one is written while attention reads the other), and an F layer's
+ *   attention shape must match the previous F layer's index tensor.
+ *   stream        sparse attention of every layer, in layer order
+ *   index_stream  every F layer's INDEXER + Top-k; layer l's indexer waits until
+ *                 the attention of layer l - 1 is done (layer l's input is
+ *                 ready), and the first attention that uses its tensor waits
+ *                 for it.  index_stream == stream runs everything in order on
+ *                 one stream (the same results).  Both streams on one device.
+ *   On return, later work enqueued on `stream` is ordered after every indexer of
+ *   the call.  The call creates and releases 2 events per F layer (host-side
+ *   runtime objects; no device memory).
+ *   ws >= indexcache_forward_mli_workspace_size(): separate regions for the
+ *   indexer stream and the attention stream.
+ */
+size_t indexcache_forward_mli_workspace_size(const char* pattern, int32_t n_layers,
+                                             const dsa_layer* layers, int32_t k);
+dsa_status indexcache_forward_mli(const char* pattern, int32_t n_layers, const dsa_layer* layers,
+                                  int32_t k, int32_t* src_layer, void* ws, size_t ws_bytes,
+                                  hipStream_t stream, hipStream_t index_stream);
+
+/*
  * Cross-layer overlap ([DSA-NOTES] §3.1; [IC-SUMMARY] Appendix A):
  * |T_a[r] ∩ T_b[r]| for rows r = 0..rows-1 of two index tensors with k columns
  * (each row ascending with -1 padding, as produced above).  row_counts
@@ -296,6 +324,26 @@ dsa_status dsa_similarity_matrix(int32_t n_layers, const dsa_layer* layers, int3
  */
 dsa_status dsa_pattern_search(const double* S, int32_t n_layers, int32_t n_full, char* pattern,
                               double* score);
+
+/*
+ * Measurement helper, not a step of the method: gather-bandwidth probe.  Reads
+ * every selected 1152-byte row (576 bf16 latent columns, the MLA layout the
+ * sparse attention gathers; [DSA-NOTES] §3) of every query's index row, as a
+ * sparse-attention pass must, with no arithmetic beyond an XOR checksum per
+ * wave.  Its rate bounds what the attention kernel's gathers can reach.
+ *   table   device [n_rows, 1152 bytes], 16-byte aligned; n_rows * 1152 < 2^31
+ *   idx     device int32 [n_q, topk]; entries outside [0, n_rows) read nothing
+ *   mode    0: four waves per query, each reading the quarter of every row the
+ *              attention kernel's wave reads (two steps of 16 rows in flight)
+ *           1: one wave per query, whole rows, 64 bytes of 16 rows per load
+ *           2: one wave per query, whole rows, the 16 rows of a step read end
+ *              to end (eight lanes per 128-byte line)
+ *           3, 4, 5: modes 0, 1, 2 with deeper prefetch (4, 3, 3 steps in flight)
+ *   out     device uint32 [dsa_gather_probe_out_words(n_q, mode)] checksums
+ */
+int64_t dsa_gather_probe_out_words(int64_t n_q, int32_t mode);
+dsa_status dsa_gather_probe(const void* table, int32_t n_rows, const int32_t* idx, int64_t n_q,
+                            int32_t topk, int32_t mode, uint32_t* out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

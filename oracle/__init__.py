@@ -10,6 +10,7 @@ Plain, slow, float64 NumPy.  Sources (web pages, cited by title and section):
                (reading notes on IndexCache, notes.kuangjux.top)
   [IC-SUMMARY] "IndexCache: Accelerating Sparse Attention via Cross-Layer Index
                Reuse" (section-by-section summary, papercache.org)
+  [MLI]        "MLI重构DeepSeek稀疏注意力：跨层复用索引免训提速" (zicq.com)
 
 Parity pins: every function here is pinned by the CPU test suite against
 worked examples printed on those pages, closed forms, library routines or
@@ -20,7 +21,7 @@ No function is unpinned.
 from .numerics import bf16_bits_to_f64, e4m3fn_codes_to_f64, dequantize  # noqa: F401
 from .dsa import (  # noqa: F401
     indexer_scores, topk_row, indexer_topk, sparse_attn, source_layers,
-    indexcache_forward, overlap, overlap_matrix, amdahl_speedup,
+    indexcache_forward, mli_source_layers, mli_forward, overlap, overlap_matrix, amdahl_speedup,
 )
 from .distill import kl_multi, kl_average, indexer_distill  # noqa: F401
 from .pattern_search import (  # noqa: F401

@@ -147,6 +147,46 @@ def indexcache_forward(pattern, indexer_fn, attn_fn):
     return src, Ts, outs, calls
 
 
+def mli_source_layers(pattern: str):
+    """Sources under the multi-layer-indexer shift ([MLI] "核心思路": a layer
+    reuses the index set the previous indexer already produced, which frees its
+    own indexer to run beside its attention), combined with IndexCache's F/S
+    pattern ([MLI] "与 IndexCache／IndexShare 的组合"): layer l attends with the
+    index tensor of the nearest F layer j < l; layer 1 has no earlier indexer
+    and uses its own.  An S layer's source is the one IndexCache gives it; an F
+    layer l > 1 takes the source IndexCache gives layer l - 1.  1-based."""
+    source_layers(pattern)                       # same validation
+    src, last = [], None
+    for l, c in enumerate(pattern, start=1):
+        src.append(l if last is None else last)
+        if c == "F":
+            last = l
+    return src
+
+
+def mli_forward(pattern, indexer_fn, attn_fn):
+    """IndexCache loop with the multi-layer-indexer shift ([MLI] "核心思路"):
+    for l = 1..N, an F layer runs its indexer (beside its attention, on
+    hardware that overlaps them); layer l's attention uses the cached index
+    tensor as it stood before layer l's indexer, except on layer 1, which has
+    none and waits for its own; then an F layer's new tensor replaces the cache.
+    Same arguments and returns as indexcache_forward."""
+    src = mli_source_layers(pattern)
+    T_cache = None
+    Ts, outs, calls = [], [], []
+    for l, c in enumerate(pattern, start=1):
+        T_new = None
+        if c == "F":
+            T_new = indexer_fn(l)
+            calls.append(l)
+        T_use = T_cache if T_cache is not None else T_new
+        Ts.append(T_use)
+        outs.append(attn_fn(l, T_use))
+        if T_new is not None:
+            T_cache = T_new
+    return src, Ts, outs, calls
+
+
 def overlap(Ta, Tb, k, rows=None):
     """overlap(i, j) = |T^(i) ∩ T^(j)| / k ([DSA-NOTES] §3.1; [IC-SUMMARY]
     Appendix A), averaged over the given rows (default: every row).  Entries

@@ -299,3 +299,31 @@ def test_binding_rejects_non_dense_layouts():
         L.sparse_attn_args(Q, kv, torch.zeros(1, 16, 4, dtype=torch.int32).transpose(1, 2), 1.0, out)
     with pytest.raises(ValueError):
         L.sparse_attn_args(Q, kv, idx, 1.0, torch.zeros(1, 4, 16, 1024)[..., :512])
+
+
+def mli_status(pattern, arr, k=16, ws=None, ws_bytes=0):
+    return L.indexcache_forward_mli_c(pattern.encode(), len(pattern), arr, k, None, ws, ws_bytes, None, None)
+
+
+def test_mli_forward_validation():
+    """The overlapped loop validates like indexcache_forward, and also refuses
+    consecutive F layers that share idx_out (one is written while attention
+    reads the other); its workspace holds separate indexer and attention
+    regions."""
+    assert mli_status("SFFF", layers("FFFF")) == 1
+    arr = layers("FSFS")
+    arr[2].idx_out = FAKE + 4096
+    need = L.indexcache_forward_mli_workspace_size(b"FSFS", 4, arr, 16)
+    assert need >= L.indexcache_forward_workspace_size(b"FSFS", 4, arr, 16) > 0
+    assert mli_status("FSFS", arr) == 3                         # workspace missing
+    assert mli_status("FSFS", arr, ws=FAKE + 8, ws_bytes=need) == 1   # misaligned workspace
+    arr[2].idx_out = arr[0].idx_out                            # consecutive F layers share a buffer
+    assert mli_status("FSFS", arr, ws=FAKE, ws_bytes=need) == 1
+    assert b"share idx_out" in L.dsa_last_error()
+    assert L.indexcache_forward_mli_workspace_size(b"FSFS", 4, arr, 16) == 0
+    arr = layers("FSFS")
+    arr[2].idx_out = FAKE + 4096
+    arr[2].sa.n_q = 5                                          # does not match layer 0's tensor
+    arr[2].ix.n_q = 5
+    arr[3].sa.n_q = 5
+    assert mli_status("FSFS", arr, ws=FAKE, ws_bytes=need) == 1

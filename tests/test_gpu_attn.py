@@ -107,3 +107,30 @@ def test_overlap_counts(dsa, dev):
     rows = np.arange(k - 1, 700)
     ov = sum(ref[r] for r in rows) / (len(rows) * k)
     assert ov == pytest.approx(oracle.overlap(an, bn, k, rows))
+
+
+@pytest.mark.parametrize("mode", range(6))
+def test_gather_probe_reads_every_selected_row(dsa, dev, mode):
+    """The gather probe (measurement helper) reads each valid selected 1152-byte
+    row exactly once per query: the XOR of its per-wave checksums equals the XOR
+    of every 32-bit word of the query's selected rows; -1 padding and entries
+    past the table read nothing.  Covers a partial last workgroup (37 queries)
+    and index rows that end mid-step (300 entries)."""
+    n_rows, n_q, topk = 5000, 37, 300
+    g = torch.Generator(device=dev)
+    g.manual_seed(mode)
+    kv = torch.randint(-(1 << 15), 1 << 15, (n_rows, 576), dtype=torch.int32, generator=g, device=dev)
+    kv = kv.to(torch.int16).view(torch.bfloat16).contiguous()
+    idx = syn.random_sorted_indices(B=1, n_q=n_q, topk=topk, q_pos0=280, n_k=n_rows, seed=5, device=dev)[0]
+    idx[3, -1] = n_rows + 7                      # past the table: read nothing
+    idx[4, 10] = -1
+    out = dsa.gather_probe(kv, idx.contiguous(), mode)
+    torch.cuda.synchronize()
+    words = kv.view(torch.int16).cpu().numpy().view(np.uint32)   # [n_rows, 288]
+    got = out.cpu().numpy().view(np.uint32)
+    ix = idx.cpu().numpy()
+    for q in range(n_q):
+        sel = ix[q][(ix[q] >= 0) & (ix[q] < n_rows)]
+        want = np.bitwise_xor.reduce(words[sel].ravel()) if sel.size else np.uint32(0)
+        have = np.bitwise_xor.reduce(got[4 * q:4 * q + 4]) if mode % 3 == 0 else got[q]
+        assert have == want, (mode, q)

@@ -369,3 +369,55 @@ def test_amdahl_example():
     s = oracle.amdahl_speedup(f, g["retained"])
     assert total / s == pytest.approx(g["after_ms"])
     assert round(s, 2) == g["speedup_printed"]
+
+
+def test_mli_shift_from_the_page():
+    """[MLI] 核心思路: with an indexer on every layer, layer L attends with layer
+    L-1's indices (layer 1 with its own); combined with IndexCache's FSSS FSSS
+    pattern, the second F layer attends with the first F layer's tensor and the
+    S layers after it with the second's."""
+    g = gold("mli_shift.json")
+    assert oracle.mli_source_layers(g["all_F_pattern"]) == g["all_F_source_layer_1based"]
+    assert oracle.mli_source_layers(g["fsss_pattern"]) == g["fsss_source_layer_1based"]
+
+
+@pytest.mark.parametrize("pattern", ["F", "FF", "FSSSFSSS", "FFSFSSF", syn.DECODE_PATTERN,
+                                     syn.SEARCHED_PATTERNS_47["1/8"]])
+def test_mli_sources_against_indexcache(pattern):
+    """Invariants tying the shift to IndexCache's sources: an S layer keeps the
+    source IndexCache gives it; an F layer l > 1 takes the source IndexCache gives
+    layer l - 1; every source except layer 1's lies strictly before its layer."""
+    ic = oracle.source_layers(pattern)
+    mli = oracle.mli_source_layers(pattern)
+    assert mli[0] == 1
+    for l in range(2, len(pattern) + 1):
+        c = pattern[l - 1]
+        assert mli[l - 1] < l
+        assert pattern[mli[l - 1] - 1] == "F"
+        assert mli[l - 1] == (ic[l - 1] if c == "S" else ic[l - 2])
+
+
+def test_mli_forward_uses_the_shifted_tensor():
+    """The loop calls the indexer on F layers only, and layer l's attention sees
+    the tensor of its shifted source, never one computed after it."""
+    pattern = "FSFFSSFS"
+    made = {}
+
+    def indexer(l):
+        made[l] = ("T", l)
+        return made[l]
+
+    seen = []
+
+    def attn(l, T):
+        assert T[1] in made                      # produced already
+        seen.append(T[1])
+        return ("O", l, T[1])
+
+    src, Ts, outs, calls = oracle.mli_forward(pattern, indexer, attn)
+    assert calls == [l for l, c in enumerate(pattern, start=1) if c == "F"]
+    assert seen == src == oracle.mli_source_layers(pattern)
+    assert [t[1] for t in Ts] == src
+    assert outs == [("O", l, s) for l, s in enumerate(src, start=1)]
+    with pytest.raises(ValueError):
+        oracle.mli_source_layers("SF")
