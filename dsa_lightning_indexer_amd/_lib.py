@@ -73,6 +73,9 @@ indexcache_forward_mli_workspace_size = _sig("indexcache_forward_mli_workspace_s
                                              P_LAYER, c_i32)
 indexcache_forward_mli_c = _sig("indexcache_forward_mli", c_i32, ctypes.c_char_p, c_i32, P_LAYER, c_i32,
                                 ctypes.POINTER(c_i32), c_vp, c_sz, c_vp, c_vp)
+indexcache_forward_noalloc_c = _sig("indexcache_forward_noalloc", c_i32, ctypes.c_char_p, c_i32, P_LAYER, c_i32,
+                                   ctypes.POINTER(c_i32), c_vp)
+NOALLOC_SCRATCH_BYTES = 64 << 20      # DSA_NOALLOC_SCRATCH_BYTES
 dsa_gather_probe_out_words = _sig("dsa_gather_probe_out_words", c_i64, c_i64, c_i32)
 dsa_gather_probe = _sig("dsa_gather_probe", c_i32, c_vp, c_i32, c_vp, c_i64, c_i32, c_i32, c_vp, c_vp)
 dsa_index_overlap = _sig("dsa_index_overlap", c_i32, c_vp, c_vp, c_i64, c_i32, c_vp, c_vp, c_vp)
@@ -86,7 +89,7 @@ dsa_pattern_search = _sig("dsa_pattern_search", c_i32, ctypes.POINTER(ctypes.c_d
 EXPORTS = ["dsa_abi_version", "dsa_status_string", "dsa_last_error", "dsa_indexer_scores",
            "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_attn_workspace_size", "dsa_sparse_attn",
            "indexcache_forward_workspace_size", "indexcache_forward", "indexcache_forward_mli_workspace_size",
-           "indexcache_forward_mli", "dsa_index_overlap",
+           "indexcache_forward_mli", "indexcache_forward_noalloc", "dsa_index_overlap",
            "dsa_indexer_distill", "dsa_row_cosine", "dsa_similarity_matrix_workspace_size",
            "dsa_similarity_matrix", "dsa_pattern_search", "dsa_gather_probe_out_words", "dsa_gather_probe"]
 

@@ -133,6 +133,16 @@ def indexcache_forward_mli(pattern, specs, k, *, index_stream=None, ws=None):
     return list(src)
 
 
+def indexcache_forward_noalloc(pattern, specs, k):
+    """indexcache_forward with the library's static per-GPU scratch instead of a
+    workspace: nothing is allocated.  Same specs and result."""
+    arr = _layers(specs, k)
+    n = len(specs)
+    src = (ctypes.c_int32 * n)()
+    L.check(L.indexcache_forward_noalloc_c(pattern.encode(), n, arr, k, src, _stream()))
+    return list(src)
+
+
 def index_overlap(a, b, k, *, rows=None, row_counts=None, total=None):
     """Adds sum_r |a[r] ∩ b[r]| to `total` (uint64 stored in an int64 tensor of one element);
     optionally writes per-row counts.  a, b: int32 [rows, k] (any leading dims flattened)."""

@@ -15,7 +15,7 @@ ARCH = os.environ.get("DSA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["select.hip", "select_few.hip", "indexer.hip", "sparse_attn.hip", "overlap.hip", "distill.hip", "similarity.hip",
-           "gather_probe.hip", "pattern_search.cpp", "api.cpp"]
+           "gather_probe.hip", "pattern_search.cpp", "api.cpp", "noalloc.hip"]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Werror", "-Wno-unused-function",
     # keep the compiler from emitting packed fp32 VALU ops

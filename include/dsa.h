@@ -208,6 +208,29 @@ dsa_status indexcache_forward_mli(const char* pattern, int32_t n_layers, const d
                                   hipStream_t stream, hipStream_t index_stream);
 
 /*
+ * indexcache_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc.  The call allocates nothing; the kernels'
+ * scratch memory (decode scores and select state, attention split partials)
+ * is one static device array of DSA_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends.
+ *   Arguments, outputs and results are those of indexcache_forward.
+ *   The first call on a device looks up that device's array (make it before
+ *   capturing a graph); the stream must belong to the current device.
+ *   Layers whose workspace need (indexcache_forward_workspace_size) exceeds
+ *   DSA_NOALLOC_SCRATCH_BYTES are rejected with DSA_ERR_WORKSPACE before
+ *   anything is enqueued: decode stacks fit (8 x 204800 keys need about
+ *   8.5 MB), prefill F layers on the fused path (537 MB of candidate slices)
+ *   do not.
+ *   Every call on one GPU shares that GPU's array: calls that overlap in time
+ *   on one GPU (two streams, two threads) race and must be serialised by the
+ *   caller.  Each call clears the state it needs before using it.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+dsa_status indexcache_forward_noalloc(const char* pattern, int32_t n_layers, const dsa_layer* layers,
+                                      int32_t k, int32_t* src_layer, hipStream_t stream);
+
+/*
  * Cross-layer overlap ([DSA-NOTES] §3.1; [IC-SUMMARY] Appendix A):
  * |T_a[r] ∩ T_b[r]| for rows r = 0..rows-1 of two index tensors with k columns
  * (each row ascending with -1 padding, as produced above).  row_counts

@@ -301,6 +301,25 @@ def test_binding_rejects_non_dense_layouts():
         L.sparse_attn_args(Q, kv, idx, 1.0, torch.zeros(1, 4, 16, 1024)[..., :512])
 
 
+def test_noalloc_rejects_before_touching_the_device():
+    """The allocation-free driver validates like indexcache_forward and refuses
+    layers whose scratch need exceeds its static array, before any device call
+    (these run on a machine without a GPU)."""
+    st = lambda pat, arr, k=16: L.indexcache_forward_noalloc_c(pat.encode(), len(pat), arr, k, None, None)
+    assert st("SFFF", layers("FFFF")) == 1
+    assert st("FSS", layers("FSS"), k=0) == 1
+    # a prefill F layer takes the fused path: 537 MB of candidate slices > 64 MiB
+    arr = one_f_layer(ix(n_q=16384, n_k=16384))
+    assert L.indexcache_forward_workspace_size(b"F", 1, arr, 16) > L.NOALLOC_SCRATCH_BYTES
+    assert st("F", arr) == 3
+    assert b"scratch" in L.dsa_last_error()
+    # a decode layer just over the limit: 8 rows x n_k fp32 scores alone exceed it
+    big = one_f_layer(ix(batch=8, n_q=1, n_k=(1 << 21) + 1024, q_pos0=(1 << 21) + 1023, dtype=L.DSA_FP8_E4M3,
+                         q_scale=FAKE, k_scale=FAKE))
+    assert L.indexcache_forward_workspace_size(b"F", 1, big, 16) > L.NOALLOC_SCRATCH_BYTES
+    assert st("F", big) == 3
+
+
 def mli_status(pattern, arr, k=16, ws=None, ws_bytes=0):
     return L.indexcache_forward_mli_c(pattern.encode(), len(pattern), arr, k, None, ws, ws_bytes, None, None)
 
