@@ -156,13 +156,16 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 // columns [128w, 128w + 128): four 32-wide K steps of Q.K and the 128 V columns
 // of its slice of the output; waves 0 and 1 also own one of the two rope K
 // steps (columns 512 + 32w ..).  Per 16-position step each wave gathers only
-// its own columns of the 16 rows (registers, two steps ahead), forms its
-// partial S^T, and the four partials meet in LDS (one barrier per step, the
-// partial buffer alternates between steps).  Every wave then runs the same
-// online softmax on the full S^T and multiplies its own V slice, staged in a
-// wave-private LDS tile and read back transposed as in sa_mla_kernel.  The
-// output accumulators are a quarter of sa_mla_kernel's, so three workgroups
-// fit on a CU.
+// its own columns of the 16 rows (registers, two steps ahead): its 256-byte V
+// slice of each row (two whole 128-byte lines) four rows per load instruction,
+// sixteen lanes per row, so every instruction fetches whole lines; the slices
+// go to a wave-private LDS tile, which serves both the K fragments of Q.K
+// (read back row-per-lane) and the transposed V fragments of P.V.  The rope
+// slice (64 bytes per row) is loaded straight in the MFMA fragment layout.
+// The four partial S^T meet in LDS (one barrier per step, the partial buffer
+// alternates between steps).  Every wave then runs the same online softmax on
+// the full S^T and multiplies its own V slice.  The output accumulators are a
+// quarter of a one-wave-per-query design's, so three workgroups fit on a CU.
 template <int DQK, int DV>
 __global__ __launch_bounds__(256, 3) void sa_mla4_kernel(SAParams p) {
   static_assert(DV % 128 == 0 && DQK - DV == 64, "latent layout: 4 V slices of 128 columns + 64 rope columns");
@@ -171,7 +174,14 @@ __global__ __launch_bounds__(256, 3) void sa_mla4_kernel(SAParams p) {
   constexpr int KSW = CW / 32;           // K steps inside the wave's V slice
   constexpr int KS = KSW + 1;            // + a rope step (waves 0 and 1)
   constexpr int NDT = CW / 16;           // output tiles of 16 columns per wave
-  constexpr int VPITCH = CW * 2 + 32;    // LDS row pitch in bytes (bank spread for the transposed reads)
+  constexpr int SLB = CW * 2;            // bytes of the wave's V slice per row
+  constexpr int LPR = SLB / 16;          // lanes (16-byte chunks) per row slice: 16
+  constexpr int RPL = 64 / LPR;          // rows per load instruction: 4
+  static_assert(LPR == 16 && kTile % RPL == 0 && KSW == kTile / RPL, "one V load per K step");
+  // LDS row pitch: 76 dwords, so the row-per-lane 16-byte fragment reads (12 r
+  // mod 64 banks) and the transposed 8-byte reads (each bank twice per 64
+  // lanes) are both conflict-free
+  constexpr int VPITCH = SLB + 48;
   __shared__ __attribute__((aligned(16))) uint8_t vt[NW][kTile * VPITCH];
   __shared__ f32x4 spart[2][NW][64];
   __shared__ int32_t sidx[kMaxTopk];      // this split's selected positions
@@ -215,29 +225,42 @@ __global__ __launch_bounds__(256, 3) void sa_mla4_kernel(SAParams p) {
     for (int e = e0 + (int)threadIdx.x; e < e1; e += NW * 64) sidx[e - e0] = ir[e];
   }
   __syncthreads();
-  uint8_t* wrow = vt[w] + col * VPITCH + 16 * g;
+  // V slice: load j holds row RPL*j + lane/16, chunk lane%16 of the slice
+  uint8_t* wrow = vt[w] + (lane / LPR) * VPITCH + 16 * (lane % LPR);
+  // K fragment of step ks: row `col`, 8 columns at 32 ks + 8 g
+  const uint8_t* frow = vt[w] + col * VPITCH + 16 * g;
   const uint8_t* rbase = vt[w] + (4 * g + (col >> 2)) * VPITCH + 8 * (col & 3);
   int pbuf = 0;
 
-  auto fetch = [&](int tb, bf16x8 (&kb)[KS], uint64_t& vm) {
-    const int e = tb + col;
+  auto pos_of = [&](int e) {
     const int32_t s = sidx[(e < e1 ? e : e1 - 1) - e0];
-    const bool valid = e < e1 && s >= 0 && s < p.n_k;
-    vm = ballot(valid);
-    const uint32_t base = valid ? (uint32_t)s * (DQK * 2) : 0x80000000u;
+    return (e < e1 && s >= 0 && s < p.n_k) ? s : -1;
+  };
+  auto fetch = [&](int tb, bf16x8 (&kb)[KS], uint64_t& vm) {
+    const int32_t sc = pos_of(tb + col);
+    vm = ballot(sc >= 0);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint32_t off = (ks < KSW || rope ? base : 0x80000000u) + (uint32_t)(kcol(ks) * 2 + 16 * g);
-      kb[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kvr, off, 0, 0));
+    for (int j = 0; j < KSW; ++j) {
+      const int32_t s = pos_of(tb + RPL * j + lane / LPR);
+      const uint32_t off = s >= 0 ? (uint32_t)s * (DQK * 2) + (uint32_t)(SLB * w + 16 * (lane % LPR)) : 0x80000000u;
+      kb[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kvr, off, 0, 0));
     }
+    // rope step in fragment layout (waves 2 and 3 read zeros without touching memory)
+    const uint32_t off = (sc >= 0 && rope) ? (uint32_t)sc * (DQK * 2) + (uint32_t)(kcol(KSW) * 2 + 16 * g)
+                                           : 0x80000000u;
+    kb[KSW] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kvr, off, 0, 0));
   };
   auto step = [&](const bf16x8 (&kb)[KS], uint64_t vm) {
+#pragma unroll
+    for (int j = 0; j < KSW; ++j) *(bf16x8*)(wrow + RPL * VPITCH * j) = kb[j];
     f32x4 acc = f32x4{};
     // (waves 2 and 3 run the rope step on zero operands: same code in every wave)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[ks], qf[ks], acc, 0, 0, 0);
-#pragma unroll
-    for (int ks = 0; ks < KSW; ++ks) *(bf16x8*)(wrow + 64 * ks) = kb[ks];
+    for (int ks = 0; ks < KSW; ++ks) {
+      const bf16x8 kf = *(const bf16x8*)(frow + 64 * ks);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], acc, 0, 0, 0);
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[KSW], qf[KSW], acc, 0, 0, 0);
     spart[pbuf][w][lane] = acc;
     sync_lds_barrier();
     // the same summation order in every wave: identical softmax state everywhere
