@@ -66,13 +66,15 @@ def parse():
                    help="one prefill F layer of a named workload instead of the bench line: the fused "
                         "indexer+Top-k (and, for the fp8 layer, its 16-head MLA sparse attention) timed with HIP "
                         "events over --kernel-reps launches; prints one JSON object")
-    p.add_argument("--profile", choices=["indexer", "attn", "copy", "gather"], default=None,
+    p.add_argument("--profile", choices=["indexer", "attn", "copy", "gather", "decode"], default=None,
                    help="counter-collection runs: 'indexer' launches only the prefill F layer's fused "
                         "indexer+Top-k (3 launches, the first a warm-up); 'attn' that layer's prefill "
                         "sparse attention (3 launches after one indexer launch); 'copy' runs a 1 GiB read + "
                         "1 GiB write elementwise kernel, the calibration for the HBM byte counters; 'gather' "
                         "times the prefill attention of that layer and the gather probe's access patterns over the "
-                        "same index tensor and latent rows, and prints one JSON object")
+                        "same index tensor and latent rows, and prints one JSON object; 'decode' runs the decode "
+                        "stack's first three F layers' indexer+Top-k (scan + select) and their attention, each on "
+                        "its own cold K cache, once each")
     return p.parse_args()
 
 
@@ -257,6 +259,21 @@ def profile_run(args, dev):
     import dsa_lightning_indexer_amd as dsa
     from synth import inputs as syn
     L = args.prefill_len
+    if args.profile == "decode":
+        B, S = args.decode_batch, args.decode_len
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)    # evicts the inputs from L2 and MALL
+        for n, l in enumerate((0, 4, 8)):
+            ix = syn.decode_layer_indexer(l, B=B, S=S, device=dev)
+            sa = syn.decode_layer_sa(l, B=B, S=S, device=dev)
+            flush.fill_(n)
+            torch.cuda.synchronize()
+            idx = dsa.topk(ix.q, ix.k, ix.w, 2048, q_scale=ix.q_scale, k_scale=ix.k_scale, q_pos0=ix.q_pos0)
+            dsa.sparse_attn(sa.q, sa.kv, idx, sa.scale, d_v=512)
+            torch.cuda.synchronize()
+            print(f"profile decode: F layer {l} (B={B}, S={S}) indexer+Top-k and attention done ({n + 1}/3)",
+                  flush=True)
+            del ix, sa, idx
+        return
     if args.profile == "gather":
         ix, sa = syn.prefill_stack_layers(L=L, n_layers=1, seed=4, device=dev)[0]
         idx = dsa.topk(ix.q, ix.k, ix.w, 2048)

@@ -149,6 +149,7 @@ __global__ __launch_bounds__(256) void sa_generic_kernel(SAParams p) {
 constexpr int kH = 16;       // query heads per latent row
 constexpr int kTile = 16;    // selected positions per step
 constexpr int kMaxTopk = DSA_MAX_TOPK;   // longest index row
+constexpr uint32_t kInvalid = 0x80000000u;   // byte offset past every latent buffer (n_k * 1152 < 2^31)
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -184,7 +185,10 @@ __global__ __launch_bounds__(256, 3) void sa_mla4_kernel(SAParams p) {
   constexpr int VPITCH = SLB + 48;
   __shared__ __attribute__((aligned(16))) uint8_t vt[NW][kTile * VPITCH];
   __shared__ f32x4 spart[2][NW][64];
-  __shared__ int32_t sidx[kMaxTopk];      // this split's selected positions
+  // this split's selected rows as byte offsets into the latent rows (kInvalid
+  // for entries outside [0, n_k) and for the padding after the split, which
+  // the fetches up to four steps past the split's end read)
+  __shared__ uint32_t sidx[kMaxTopk + 5 * kTile];
 
   const int lane = threadIdx.x & 63;
   const int w = wave_id();
@@ -204,11 +208,17 @@ __global__ __launch_bounds__(256, 3) void sa_mla4_kernel(SAParams p) {
   const __bf16* qrow = (const __bf16*)p.q + (gi * kH + col) * (int64_t)DQK;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    qf[ks] = (ks < KSW || rope) ? *(const bf16x8*)(qrow + kcol(ks) + 8 * g) : bf16x8{};
+    qf[ks] = (ks < KSW || rope) ? __builtin_nontemporal_load((const bf16x8*)(qrow + kcol(ks) + 8 * g)) : bf16x8{};
 
   f32x4 o[NDT];
 #pragma unroll
   for (int d = 0; d < NDT; ++d) o[d] = f32x4{};
+  // Online softmax in base 2 with a lazily moved reference: scores are scaled
+  // by scale * log2 e, and the reference m_run (per head) only moves when a
+  // step's maximum exceeds it by more than kLazy, so the weights exp2(z - m_run)
+  // stay below 2^kLazy and O and l are rescaled only on those steps (a handful
+  // per row instead of every step that raises the maximum).  O / l is the same.
+  constexpr float kLazy = 8.f;
   float m_run = -__builtin_inff(), l_run = 0.f;
   const float sl2 = p.scale * 1.4426950408889634f;   // scale * log2(e)
 
@@ -222,7 +232,10 @@ __global__ __launch_bounds__(256, 3) void sa_mla4_kernel(SAParams p) {
       (int)((int64_t)p.n_k * DQK * 2), 0x00020000);
   {
     const int32_t* ir = p.idx + gi * (int64_t)p.topk;
-    for (int e = e0 + (int)threadIdx.x; e < e1; e += NW * 64) sidx[e - e0] = ir[e];
+    for (int e = e0 + (int)threadIdx.x; e < e1 + 5 * kTile; e += NW * 64) {
+      const int32_t s = e < e1 ? ir[e] : -1;
+      sidx[e - e0] = (s >= 0 && s < p.n_k) ? (uint32_t)s * (DQK * 2) : kInvalid;
+    }
   }
   __syncthreads();
   // V slice: load j holds row RPL*j + lane/16, chunk lane%16 of the slice
@@ -232,23 +245,21 @@ __global__ __launch_bounds__(256, 3) void sa_mla4_kernel(SAParams p) {
   const uint8_t* rbase = vt[w] + (4 * g + (col >> 2)) * VPITCH + 8 * (col & 3);
   int pbuf = 0;
 
-  auto pos_of = [&](int e) {
-    const int32_t s = sidx[(e < e1 ? e : e1 - 1) - e0];
-    return (e < e1 && s >= 0 && s < p.n_k) ? s : -1;
-  };
+  // (an invalid entry's offset plus a column offset stays past the buffer range)
+  const uint32_t vcol = (uint32_t)(SLB * w + 16 * (lane % LPR));
+  const uint32_t rcol = (uint32_t)(kcol(KSW) * 2 + 16 * g);
   auto fetch = [&](int tb, bf16x8 (&kb)[KS], uint64_t& vm) {
-    const int32_t sc = pos_of(tb + col);
-    vm = ballot(sc >= 0);
+    const uint32_t* si = sidx + (tb - e0);
+    const uint32_t oc = si[col];
+    vm = ballot(oc != kInvalid);
 #pragma unroll
     for (int j = 0; j < KSW; ++j) {
-      const int32_t s = pos_of(tb + RPL * j + lane / LPR);
-      const uint32_t off = s >= 0 ? (uint32_t)s * (DQK * 2) + (uint32_t)(SLB * w + 16 * (lane % LPR)) : 0x80000000u;
+      const uint32_t off = si[RPL * j + lane / LPR] + vcol;
       kb[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kvr, off, 0, 0));
     }
     // rope step in fragment layout (waves 2 and 3 read zeros without touching memory)
-    const uint32_t off = (sc >= 0 && rope) ? (uint32_t)sc * (DQK * 2) + (uint32_t)(kcol(KSW) * 2 + 16 * g)
-                                           : 0x80000000u;
-    kb[KSW] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kvr, off, 0, 0));
+    const uint32_t roff = rope ? oc + rcol : kInvalid;
+    kb[KSW] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kvr, roff, 0, 0));
   };
   auto step = [&](const bf16x8 (&kb)[KS], uint64_t vm) {
 #pragma unroll
@@ -273,22 +284,24 @@ __global__ __launch_bounds__(256, 3) void sa_mla4_kernel(SAParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) z[i] = ((vb >> i) & 1u) ? sc[i] * sl2 : -__builtin_inff();
     const float mx = quad_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
-    const float m_new = fmaxf(m_run, mx);
-    bf16x4 pb_hi = bf16x4{}, pb_lo = bf16x4{};
-    float alpha = 1.f;
-    if (m_new != -__builtin_inff()) {
-      alpha = (m_run == m_new) ? 1.f : ((m_run == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new));
-      float pe[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pe[i] = z[i] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(z[i] - m_new);
-      split_bf16(pe, pb_hi, pb_lo);
-      l_run = l_run * alpha + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
-      m_run = m_new;
-    }
-    if (ballot(alpha != 1.f)) {
+    // (also true on the first valid step, while m_run is still -inf)
+    const bool bump = mx > m_run + kLazy;
+    if (ballot(bump)) {
+      const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;   // 0 on the first step
+      m_run = bump ? mx : m_run;
+      l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
     }
+    // invalid positions have z = -inf and weight exp2(-inf) = 0; before the
+    // first valid position the reference is -inf, taken as -FLT_MAX here
+    const float mref = fmaxf(m_run, -__FLT_MAX__);
+    float pe[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pe[i] = __builtin_amdgcn_exp2f(z[i] - mref);
+    bf16x4 pb_hi, pb_lo;
+    split_bf16(pe, pb_hi, pb_lo);
+    l_run += (pe[0] + pe[1]) + (pe[2] + pe[3]);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(rbase + 32 * dt));
@@ -323,7 +336,7 @@ __global__ __launch_bounds__(256, 3) void sa_mla4_kernel(SAParams p) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     float* out = p.out + (gi * kH + col) * (int64_t)DV + CW * w + 4 * g;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) *(f32x4*)(out + 16 * dt) = o[dt] * inv;
+    for (int dt = 0; dt < NDT; ++dt) __builtin_nontemporal_store(o[dt] * inv, (f32x4*)(out + 16 * dt));
   } else {
     float* wo = p.ws_o + ((gi * p.nsplit + split) * kH + col) * (int64_t)DV + CW * w + 4 * g;
 #pragma unroll
