@@ -53,8 +53,8 @@ def test_abi_host_code_is_clean_under_asan_and_ubsan(tmp_path):
     assert r.returncode == 0, r.stderr
     exe = str(tmp_path / "abi_checks")
     # link line: no -Xarch_ option, so the sanitizers are kept off the device side explicitly
-    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-fsanitize=address", "-fsanitize=undefined",
-                        "-fno-gpu-sanitize", main_o, *objs, "-o", exe, "-L/opt/rocm/lib", "-lamdhip64"],
+    link = [HIPCC, "--offload-arch=gfx950", "-fno-gpu-sanitize", "-fsanitize=address", "-fsanitize=undefined"]
+    r = subprocess.run([*link, main_o, *objs, "-o", exe, "-L/opt/rocm/lib", "-lamdhip64"],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1",
