@@ -66,7 +66,7 @@ def parse():
                    help="one prefill F layer of a named workload instead of the bench line: the fused "
                         "indexer+Top-k (and, for the fp8 layer, its 16-head MLA sparse attention) timed with HIP "
                         "events over --kernel-reps launches; prints one JSON object")
-    p.add_argument("--profile", choices=["indexer", "attn", "copy", "gather", "decode"], default=None,
+    p.add_argument("--profile", choices=["indexer", "attn", "copy", "gather", "decode", "stream"], default=None,
                    help="counter-collection runs: 'indexer' launches only the prefill F layer's fused "
                         "indexer+Top-k (3 launches, the first a warm-up); 'attn' that layer's prefill "
                         "sparse attention (3 launches after one indexer launch); 'copy' runs a 1 GiB read + "
@@ -74,7 +74,9 @@ def parse():
                         "times the prefill attention of that layer and the gather probe's access patterns over the "
                         "same index tensor and latent rows, and prints one JSON object; 'decode' runs the decode "
                         "stack's first three F layers' indexer+Top-k (scan + select) and their attention, each on "
-                        "its own cold K cache, once each")
+                        "its own cold K cache, once each; 'stream' times the decode scan of one F layer on a cold "
+                        "cache (evicted by a 1 GiB write right before, no host sync between) against the gather "
+                        "probe reading the same number of bytes in order, also cold, and prints one JSON object")
     return p.parse_args()
 
 
@@ -259,6 +261,44 @@ def profile_run(args, dev):
     import dsa_lightning_indexer_amd as dsa
     from synth import inputs as syn
     L = args.prefill_len
+    if args.profile == "stream":
+        B, S = args.decode_batch, args.decode_len
+        ix = syn.decode_layer_indexer(0, B=B, S=S, device=dev)
+        scores = torch.empty((B, 1, 2048), dtype=torch.int32, device=dev)
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        nbytes = B * S * (128 + 4)
+        # the same bytes as rows of 1152 B read in position order, 64 rows per probe "query"
+        rows = nbytes // 1152 // 64 * 64
+        table = torch.empty(rows * 1152, dtype=torch.uint8, device=dev).view(rows, 1152)
+        table.fill_(1)
+        seq = torch.arange(rows, dtype=torch.int32, device=dev).view(-1, 64)
+        st = torch.cuda.current_stream()
+
+        def cold(fn, reps=7):
+            ts = []
+            for _ in range(reps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                flush.fill_(0)
+                a.record(st)
+                fn()
+                b.record(st)
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            return sorted(ts)[len(ts) // 2]
+        scan = lambda: dsa.topk(ix.q, ix.k, ix.w, 2048, q_scale=ix.q_scale, k_scale=ix.k_scale,
+                                q_pos0=ix.q_pos0, out=scores)
+        scan()
+        for m in (2, 5):
+            dsa.gather_probe(table, seq, m)
+        torch.cuda.synchronize()
+        res = {"workload": f"decode F layer B={B} x S={S} fp8 K cache ({nbytes} B of keys and scales), cold",
+               "decode_indexer_topk_ms": cold(scan)}
+        for m in (2, 5):
+            ms = cold(lambda: dsa.gather_probe(table, seq, m))
+            res[f"probe_mode{m}_ms"] = ms
+            res[f"probe_mode{m}_GBs"] = rows * 1152 / (ms * 1e-3) / 1e9
+        print(json.dumps(res), flush=True)
+        return
     if args.profile == "decode":
         B, S = args.decode_batch, args.decode_len
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)    # evicts the inputs from L2 and MALL
