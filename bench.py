@@ -75,7 +75,7 @@ def parse():
                         "same index tensor and latent rows, and prints one JSON object; 'decode' runs the decode "
                         "stack's first three F layers' indexer+Top-k (scan + select) and their attention, each on "
                         "its own cold K cache, once each; 'stream' times the decode scan of one F layer on a cold "
-                        "cache (evicted by a 1 GiB write right before, no host sync between) against the gather "
+                        "cache (evicted by a 1 GiB read right before, no host sync between) against the gather "
                         "probe reading the same number of bytes in order, also cold, and prints one JSON object")
     return p.parse_args()
 
@@ -265,7 +265,13 @@ def profile_run(args, dev):
         B, S = args.decode_batch, args.decode_len
         ix = syn.decode_layer_indexer(0, B=B, S=S, device=dev)
         scores = torch.empty((B, 1, 2048), dtype=torch.int32, device=dev)
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # eviction by a 1 GiB read (written once, long before): it leaves clean lines behind, as
+        # the stack does (a large write right before would leave the cache full of dirty lines
+        # whose write-back halves the scan's read rate)
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        flush_sum = torch.empty((), dtype=torch.float32, device=dev)
+        for _ in range(2):
+            torch.sum(flush, dim=0, out=flush_sum)
         nbytes = B * S * (128 + 4)
         # the same bytes as rows of 1152 B read in position order, 64 rows per probe "query"
         rows = nbytes // 1152 // 64 * 64
@@ -278,7 +284,7 @@ def profile_run(args, dev):
             ts = []
             for _ in range(reps):
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                flush.fill_(0)
+                torch.sum(flush, dim=0, out=flush_sum)
                 a.record(st)
                 fn()
                 b.record(st)
@@ -293,6 +299,20 @@ def profile_run(args, dev):
         torch.cuda.synchronize()
         res = {"workload": f"decode F layer B={B} x S={S} fp8 K cache ({nbytes} B of keys and scales), cold",
                "decode_indexer_topk_ms": cold(scan)}
+        # the streaming read probe over the same number of bytes, over grid sizes and depths
+        sbytes = nbytes // 16384 * 16384
+        sbuf = torch.ones(sbytes // 4, dtype=torch.int32, device=dev)
+        best = None
+        for wgs in (512, 1024, 2048, 4096):
+            for unroll in (1, 2, 4):
+                dsa.stream_probe(sbuf, wgs, unroll)
+                ms = cold(lambda: dsa.stream_probe(sbuf, wgs, unroll), reps=5)
+                gbs = sbytes / (ms * 1e-3) / 1e9
+                res[f"stream_wg{wgs}_u{unroll}_GBs"] = gbs
+                if best is None or gbs > best[2]:
+                    best = (wgs, unroll, gbs, ms)
+        res["stream_best"] = {"workgroups": best[0], "unroll": best[1], "GBs": best[2], "ms": best[3],
+                              "bytes": sbytes}
         for m in (2, 5):
             ms = cold(lambda: dsa.gather_probe(table, seq, m))
             res[f"probe_mode{m}_ms"] = ms

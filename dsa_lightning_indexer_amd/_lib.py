@@ -78,6 +78,7 @@ indexcache_forward_noalloc_c = _sig("indexcache_forward_noalloc", c_i32, ctypes.
 NOALLOC_SCRATCH_BYTES = 64 << 20      # DSA_NOALLOC_SCRATCH_BYTES
 dsa_gather_probe_out_words = _sig("dsa_gather_probe_out_words", c_i64, c_i64, c_i32)
 dsa_gather_probe = _sig("dsa_gather_probe", c_i32, c_vp, c_i32, c_vp, c_i64, c_i32, c_i32, c_vp, c_vp)
+dsa_stream_probe = _sig("dsa_stream_probe", c_i32, c_vp, c_i64, c_i32, c_i32, c_vp, c_vp)
 dsa_index_overlap = _sig("dsa_index_overlap", c_i32, c_vp, c_vp, c_i64, c_i32, c_vp, c_vp, c_vp)
 dsa_indexer_distill = _sig("dsa_indexer_distill", c_i32, ctypes.POINTER(DistillArgs), c_vp)
 dsa_row_cosine = _sig("dsa_row_cosine", c_i32, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp)
@@ -91,7 +92,8 @@ EXPORTS = ["dsa_abi_version", "dsa_status_string", "dsa_last_error", "dsa_indexe
            "indexcache_forward_workspace_size", "indexcache_forward", "indexcache_forward_mli_workspace_size",
            "indexcache_forward_mli", "indexcache_forward_noalloc", "dsa_index_overlap",
            "dsa_indexer_distill", "dsa_row_cosine", "dsa_similarity_matrix_workspace_size",
-           "dsa_similarity_matrix", "dsa_pattern_search", "dsa_gather_probe_out_words", "dsa_gather_probe"]
+           "dsa_similarity_matrix", "dsa_pattern_search", "dsa_gather_probe_out_words", "dsa_gather_probe",
+           "dsa_stream_probe"]
 
 
 class DsaError(RuntimeError):

@@ -270,3 +270,15 @@ def gather_probe(kv, idx, mode, *, out=None):
         out = torch.empty(max(words, 1), dtype=torch.int32, device=kv.device)
     L.check(L.dsa_gather_probe(kv.data_ptr(), n_rows, idx2.data_ptr(), n_q, topk, mode, out.data_ptr(), _stream()))
     return out
+
+
+def stream_probe(buf, workgroups, unroll, *, out=None):
+    """Measurement helper: read the contiguous device buffer `buf` (its bytes a
+    multiple of 16384) once in order with `workgroups` workgroups and `unroll`
+    16-KiB chunks in flight per wave; returns the uint32 checksums (as int32)."""
+    L._dense("buf", buf)
+    nbytes = buf.numel() * buf.element_size()
+    if out is None:
+        out = torch.empty(4 * workgroups, dtype=torch.int32, device=buf.device)
+    L.check(L.dsa_stream_probe(buf.data_ptr(), nbytes, workgroups, unroll, out.data_ptr(), _stream()))
+    return out

@@ -648,6 +648,19 @@ dsa_status dsa_gather_probe(const void* table, int32_t n_rows, const int32_t* id
   return hip_status(dsa_host::gather_probe_launch(table, n_rows, idx, n_q, topk, mode, out, stream), "probe launch");
 }
 
+dsa_status dsa_stream_probe(const void* buf, int64_t bytes, int32_t workgroups, int32_t unroll, uint32_t* out,
+                            hipStream_t stream) {
+  g_last_error.clear();
+  const int64_t chunk = dsa_host::stream_probe_chunk_bytes();
+  if (!buf || !out) return fail(DSA_ERR_INVALID, "buf and out are required");
+  if (!aligned(buf, 16) || !aligned(out, 4)) return fail(DSA_ERR_INVALID, "buf must be 16-byte aligned, out 4-byte");
+  if (bytes < chunk || bytes % chunk != 0 || bytes >= ((int64_t)1 << 31))
+    return fail(DSA_ERR_INVALID, "bytes must be a positive multiple of %lld below 2^31", (long long)chunk);
+  if (workgroups < 1 || workgroups > 65536) return fail(DSA_ERR_INVALID, "workgroups must be 1..65536");
+  if (unroll != 1 && unroll != 2 && unroll != 4) return fail(DSA_ERR_INVALID, "unroll must be 1, 2 or 4");
+  return hip_status(dsa_host::stream_probe_launch(buf, bytes / chunk, workgroups, unroll, out, stream), "probe launch");
+}
+
 dsa_status dsa_pattern_search(const double* S, int32_t n, int32_t n_full, char* pattern, double* score) {
   g_last_error.clear();
   if (n < 1 || n > 1024) return fail(DSA_ERR_INVALID, "n_layers must be 1..1024");

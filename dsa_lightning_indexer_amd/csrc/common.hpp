@@ -152,6 +152,11 @@ int64_t gather_probe_out_words(int64_t n_q, int32_t mode);
 hipError_t gather_probe_launch(const void* table, int32_t n_rows, const int32_t* idx, int64_t n_q, int32_t topk,
                                int32_t mode, uint32_t* out, hipStream_t s);
 
+// Streaming read probe over a contiguous buffer of 16-KiB chunks (gather_probe.hip).
+int64_t stream_probe_chunk_bytes();
+hipError_t stream_probe_launch(const void* buf, int64_t nchunks, int32_t wgs, int32_t unroll, uint32_t* out,
+                               hipStream_t s);
+
 // indexcache_forward's validation and workspace need (api.cpp).
 dsa_status forward_workspace_need(const char* pattern, int32_t n, const dsa_layer* layers, int32_t k, size_t* need);
 // Sets the thread-local text dsa_last_error() returns (api.cpp) and returns st.

@@ -156,3 +156,64 @@ hipError_t gather_probe_launch(const void* table, int32_t n_rows, const int32_t*
 }
 
 }  // namespace dsa_host
+
+// ---------------------------------------------------------------- streaming read probe
+// Reads a contiguous buffer once, in order, with no arithmetic beyond an XOR
+// checksum per wave: the rate bounds what a scan over the same bytes (the decode
+// indexer's K cache) can reach.  Workgroup x reads 16-KiB chunks x, x + G,
+// x + 2G, ... (G workgroups); each lane issues four 16-byte loads per chunk, and
+// UNROLL chunks are in flight per wave.
+namespace {
+
+constexpr int kStreamChunk = 256 * 64;      // bytes per workgroup per chunk: 256 lanes x 4 x 16 B
+
+template <int UNROLL>
+__global__ __launch_bounds__(256) void stream_probe_kernel(const uint8_t* buf, uint32_t nchunks, uint32_t* out) {
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id();
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(buf), (short)0, (int)(nchunks * (uint32_t)kStreamChunk),
+                                        0x00020000);
+  uint32_t acc = 0;
+  // within a chunk: wave w reads its 4 KiB (4 loads of 64 lanes x 16 B, 1 KiB each)
+  const uint32_t lofs = (uint32_t)(w * 4096 + 16 * lane);
+  for (uint32_t c0 = blockIdx.x; c0 < nchunks; c0 += gridDim.x * UNROLL) {
+    u32x4 v[UNROLL][4];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const uint32_t c = c0 + (uint32_t)u * gridDim.x;
+      // past the end: an offset beyond the range reads zeros without touching memory
+      const uint32_t base = c < nchunks ? c * (uint32_t)kStreamChunk + lofs : 0x80000000u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v[u][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, base + 1024u * j, 0, 0));
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc ^= xor4(v[u][j]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o, 64);
+  if (lane == 0) out[blockIdx.x * 4 + w] = acc;
+}
+
+}  // namespace
+
+namespace dsa_host {
+
+int64_t stream_probe_chunk_bytes() { return kStreamChunk; }
+
+hipError_t stream_probe_launch(const void* buf, int64_t nchunks, int32_t wgs, int32_t unroll, uint32_t* out,
+                               hipStream_t s) {
+  const uint8_t* b = (const uint8_t*)buf;
+  switch (unroll) {
+    case 1: hipLaunchKernelGGL(stream_probe_kernel<1>, dim3((unsigned)wgs), dim3(256), 0, s, b, (uint32_t)nchunks, out); break;
+    case 2: hipLaunchKernelGGL(stream_probe_kernel<2>, dim3((unsigned)wgs), dim3(256), 0, s, b, (uint32_t)nchunks, out); break;
+    case 4: hipLaunchKernelGGL(stream_probe_kernel<4>, dim3((unsigned)wgs), dim3(256), 0, s, b, (uint32_t)nchunks, out); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsa_host

@@ -368,6 +368,19 @@ int64_t dsa_gather_probe_out_words(int64_t n_q, int32_t mode);
 dsa_status dsa_gather_probe(const void* table, int32_t n_rows, const int32_t* idx, int64_t n_q,
                             int32_t topk, int32_t mode, uint32_t* out, hipStream_t stream);
 
+/*
+ * Measurement helper, not a step of the method: streaming read probe.  Reads
+ * `bytes` of a contiguous device buffer once, in order, with no arithmetic
+ * beyond an XOR checksum per wave; its rate bounds what a scan of the same
+ * bytes (the decode indexer's K cache) can reach.  Workgroup x (of
+ * `workgroups`, 256 threads each) reads 16-KiB chunks x, x + G, x + 2G, ...,
+ * with `unroll` (1, 2 or 4) chunks in flight per wave.
+ *   buf    device, 16-byte aligned; bytes a multiple of 16384, below 2^31
+ *   out    device uint32 [4 * workgroups] checksums
+ */
+dsa_status dsa_stream_probe(const void* buf, int64_t bytes, int32_t workgroups, int32_t unroll,
+                            uint32_t* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -134,3 +134,19 @@ def test_gather_probe_reads_every_selected_row(dsa, dev, mode):
         want = np.bitwise_xor.reduce(words[sel].ravel()) if sel.size else np.uint32(0)
         have = np.bitwise_xor.reduce(got[4 * q:4 * q + 4]) if mode % 3 == 0 else got[q]
         assert have == want, (mode, q)
+
+
+@pytest.mark.parametrize("wgs,unroll", [(1, 1), (7, 2), (300, 4), (4096, 4)])
+def test_stream_probe_reads_every_byte_once(dsa, dev, wgs, unroll):
+    """The streaming read probe (measurement helper) reads the whole buffer
+    exactly once: the XOR of its per-wave checksums equals the XOR of every
+    32-bit word, for grids smaller and larger than the number of chunks."""
+    n = 16384 * 101
+    g = torch.Generator(device=dev)
+    g.manual_seed(wgs)
+    buf = torch.randint(-(1 << 30), 1 << 30, (n // 4,), dtype=torch.int32, generator=g, device=dev)
+    out = dsa.stream_probe(buf, wgs, unroll)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(buf.cpu().numpy().view(np.uint32))
+    have = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+    assert have == want
