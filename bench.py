@@ -66,7 +66,8 @@ def parse():
                    help="one prefill F layer of a named workload instead of the bench line: the fused "
                         "indexer+Top-k (and, for the fp8 layer, its 16-head MLA sparse attention) timed with HIP "
                         "events over --kernel-reps launches; prints one JSON object")
-    p.add_argument("--profile", choices=["indexer", "attn", "copy", "gather", "decode", "stream"], default=None,
+    p.add_argument("--profile", choices=["indexer", "indexer_fp8", "attn", "copy", "gather", "decode", "stream"],
+                   default=None,
                    help="counter-collection runs: 'indexer' launches only the prefill F layer's fused "
                         "indexer+Top-k (3 launches, the first a warm-up); 'attn' that layer's prefill "
                         "sparse attention (3 launches after one indexer launch); 'copy' runs a 1 GiB read + "
@@ -261,6 +262,17 @@ def profile_run(args, dev):
     import dsa_lightning_indexer_amd as dsa
     from synth import inputs as syn
     L = args.prefill_len
+    if args.profile == "indexer_fp8":
+        c = syn.WORKLOADS["prefill_fp8_L65536"]
+        ix = syn.indexer_inputs(B=1, n_q=c["L"], H=c["H"], d=c["d"], dtype=c["dtype"], values=c["values"],
+                                w_dist=c["w_dist"], seed=c["seed"], device=dev)
+        out = torch.empty((1, c["L"], c["topk"]), dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+        for i in range(3):
+            dsa.topk(ix.q, ix.k, ix.w, c["topk"], q_scale=ix.q_scale, k_scale=ix.k_scale, out=out)
+            torch.cuda.synchronize()
+            print(f"profile indexer_fp8: fused indexer+Top-k L={c['L']} launch {i + 1}/3 done", flush=True)
+        return
     if args.profile == "stream":
         B, S = args.decode_batch, args.decode_len
         ix = syn.decode_layer_indexer(0, B=B, S=S, device=dev)
