@@ -174,7 +174,8 @@ PROBE_MODES = {0: "quarter rows, 2 steps in flight (the attention kernel's patte
                2: "whole rows per wave, rows end to end, 2 steps",
                3: "quarter rows, 4 steps in flight",
                4: "whole rows per wave, 64 B of 16 rows per load, 3 steps",
-               5: "whole rows per wave, rows end to end, 3 steps"}
+               5: "whole rows per wave, rows end to end, 3 steps",
+               6: "the attention kernel's pattern: 256-B V slices of 4 rows per load + rope, 2 steps"}
 
 
 def gather_ceiling(dsa, kv, idx, reps):

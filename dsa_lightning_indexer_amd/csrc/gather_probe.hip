@@ -17,6 +17,10 @@
 // mode + 3: the same pattern with deeper prefetch: four steps in flight for
 //           quarter rows, three for whole rows (four would not fit the
 //           register file).
+//   mode 6  the attention kernel's own pattern: one query per four-wave
+//           workgroup; wave w reads its 256-byte V slice of four rows per load
+//           instruction (whole lines) and, for w < 2, the 64-byte rope slice of
+//           16 rows (two steps in flight)
 #include "common.hpp"
 
 namespace {
@@ -75,6 +79,20 @@ struct Pattern<2> {
     return rowbase + 16 * ((64 * j + lane) % kChunks);
   }
   __device__ static int row_of(int lane, int j) { return (64 * j + lane) / kChunks; }
+};
+
+// the attention kernel's own pattern: per wave, its 256-byte V slice of four rows
+// per load instruction (16 lanes per row, whole lines), then (waves 0 and 1) the
+// 64-byte rope slice of 16 rows in the MFMA fragment layout
+template <>
+struct Pattern<3> {
+  static constexpr int kLoads = 5;
+  static constexpr int kQueriesPerWg = 1;
+  __device__ static uint32_t offset(int w, int lane, int j, uint32_t rowbase) {
+    if (j < 4) return rowbase + 256 * w + 16 * (lane & 15);
+    return w < 2 ? rowbase + 1024 + 64 * w + 16 * (lane >> 4) : 0x80000000u;
+  }
+  __device__ static int row_of(int lane, int j) { return j < 4 ? 4 * j + (lane >> 4) : (lane & 15); }
 };
 
 template <int MODE, int DEPTH>
@@ -136,7 +154,7 @@ void launch(const ProbeParams& p, hipStream_t s) {
 namespace dsa_host {
 
 int64_t gather_probe_out_words(int64_t n_q, int32_t mode) {
-  const int qw = (mode % 3) == 0 ? 1 : 4;
+  const int qw = (mode == 6 || mode % 3 == 0) ? 1 : 4;
   return (n_q + qw - 1) / qw * 4;
 }
 
@@ -150,6 +168,7 @@ hipError_t gather_probe_launch(const void* table, int32_t n_rows, const int32_t*
     case 3: launch<0, 4>(p, s); break;
     case 4: launch<1, 3>(p, s); break;
     case 5: launch<2, 3>(p, s); break;
+    case 6: launch<3, 2>(p, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

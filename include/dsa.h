@@ -362,6 +362,9 @@ dsa_status dsa_pattern_search(const double* S, int32_t n_layers, int32_t n_full,
  *           2: one wave per query, whole rows, the 16 rows of a step read end
  *              to end (eight lanes per 128-byte line)
  *           3, 4, 5: modes 0, 1, 2 with deeper prefetch (4, 3, 3 steps in flight)
+ *           6: four waves per query reading as the attention kernel does: a
+ *              wave's 256-byte V slice of four rows per load (whole lines),
+ *              then the 64-byte rope slice of 16 rows (two steps in flight)
  *   out     device uint32 [dsa_gather_probe_out_words(n_q, mode)] checksums
  */
 int64_t dsa_gather_probe_out_words(int64_t n_q, int32_t mode);
