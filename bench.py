@@ -175,7 +175,10 @@ PROBE_MODES = {0: "quarter rows, 2 steps in flight (the attention kernel's patte
                3: "quarter rows, 4 steps in flight",
                4: "whole rows per wave, 64 B of 16 rows per load, 3 steps",
                5: "whole rows per wave, rows end to end, 3 steps",
-               6: "the attention kernel's pattern: 256-B V slices of 4 rows per load + rope, 2 steps"}
+               6: "the attention kernel's pattern: 256-B V slices of 4 rows per load + rope, 2 steps",
+               7: "mode 6 with each rope line read whole by one wave (rows 4w..4w+3)",
+               8: "four waves per query, wave w reads rows 4w..4w+3 whole, end to end",
+               9: "the one-wave-per-query attention pattern: one instruction per row's V KiB + 2 rope-line loads, 2 steps"}
 
 
 def gather_ceiling(dsa, kv, idx, reps):
@@ -204,7 +207,7 @@ def sa_roofline(sa_ms, n_sel, probe):
     ceiling = probe[best_mode][1]
     tflops = flop / (sa_ms * 1e-3) / 1e12
     return {
-        "kernel": "sa_mla4_kernel (prefill sparse attention, bf16 MLA 16 heads 576/512)",
+        "kernel": "sa_mla1_kernel (prefill sparse attention, bf16 MLA 16 heads 576/512, one wave per query row)",
         "bound": "gather", "achieved": gbs, "peak": ceiling, "unit": "GB/s", "frac": gbs / ceiling,
         "peak_source": f"gather probe, best pattern: mode {best_mode} ({PROBE_MODES[best_mode]}), measured live "
                        "on the same index tensor and latent rows",
@@ -567,7 +570,7 @@ def similarity_run(args, dev):
         "kernels": {"sparse_attn_ms": sa_ms, "sparse_attn_gathered_TBps": gather / (sa_ms * 1e-3) / 1e12,
                     "row_cosine_plus_mean_us": cos_ms * 1e3, "row_cosine_GBps": cos_bytes / (cos_ms * 1e-3) / 1e9,
                     "launches_per_matrix": {"topk": n, "sparse_attn": n - 1 + pairs, "row_cosine+mean": pairs}},
-        "roofline": {"bound": "hbm", "kernel": "sa_mla4_kernel (one layer pair)",
+        "roofline": {"bound": "hbm", "kernel": "sa_mla1_kernel (one layer pair)",
                      "achieved": gather / (sa_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gather / (sa_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                      "algorithmic_per_launch": f"{sel} selected (row, position) pairs x 1152 B = {gather:.4g} B",

@@ -21,6 +21,16 @@
 //           workgroup; wave w reads its 256-byte V slice of four rows per load
 //           instruction (whole lines) and, for w < 2, the 64-byte rope slice of
 //           16 rows (two steps in flight)
+//   mode 7  mode 6 with the rope line split by rows instead of columns: wave w
+//           reads the whole 128-byte rope line of rows 4w..4w+3 (one request per
+//           line instead of two)
+//   mode 8  one query per four-wave workgroup, whole rows end to end: wave w
+//           reads rows 4w..4w+3 of each step (4.5 KiB, the last load half
+//           full), as mode 2 does for all 16 rows
+//   mode 9  the one-wave-per-query attention kernel's pattern: one query per
+//           wave; per step one load instruction per row for its first KiB (64
+//           lanes, that row alone) and two for the 16 rope lines (eight rows
+//           per instruction, eight lanes per line), two steps in flight
 #include "common.hpp"
 
 namespace {
@@ -56,7 +66,7 @@ struct Pattern<0> {
     if (j < 4) return rowbase + 256 * w + 64 * j + 16 * g;
     return w < 2 ? rowbase + 1024 + 64 * w + 16 * g : 0x80000000u;
   }
-  __device__ static int row_of(int lane, int) { return lane & 15; }
+  __device__ static int row_of(int, int lane, int) { return lane & 15; }
 };
 
 // whole rows, 64 bytes of 16 rows per instruction
@@ -67,7 +77,7 @@ struct Pattern<1> {
   __device__ static uint32_t offset(int, int lane, int j, uint32_t rowbase) {
     return rowbase + 64 * j + 16 * (lane >> 4);
   }
-  __device__ static int row_of(int lane, int) { return lane & 15; }
+  __device__ static int row_of(int, int lane, int) { return lane & 15; }
 };
 
 // whole rows end to end: chunk c = 64 j + lane of the step's 16 x 72 chunks
@@ -78,7 +88,7 @@ struct Pattern<2> {
   __device__ static uint32_t offset(int, int lane, int j, uint32_t rowbase) {
     return rowbase + 16 * ((64 * j + lane) % kChunks);
   }
-  __device__ static int row_of(int lane, int j) { return (64 * j + lane) / kChunks; }
+  __device__ static int row_of(int, int lane, int j) { return (64 * j + lane) / kChunks; }
 };
 
 // the attention kernel's own pattern: per wave, its 256-byte V slice of four rows
@@ -92,7 +102,48 @@ struct Pattern<3> {
     if (j < 4) return rowbase + 256 * w + 16 * (lane & 15);
     return w < 2 ? rowbase + 1024 + 64 * w + 16 * (lane >> 4) : 0x80000000u;
   }
-  __device__ static int row_of(int lane, int j) { return j < 4 ? 4 * j + (lane >> 4) : (lane & 15); }
+  __device__ static int row_of(int, int lane, int j) { return j < 4 ? 4 * j + (lane >> 4) : (lane & 15); }
+};
+
+// the attention pattern with each row's rope line read whole, by one wave: wave w
+// reads the 128-byte rope lines of rows 4w..4w+3 (lanes 0..31, eight per line)
+template <>
+struct Pattern<4> {
+  static constexpr int kLoads = 5;
+  static constexpr int kQueriesPerWg = 1;
+  __device__ static uint32_t offset(int w, int lane, int j, uint32_t rowbase) {
+    if (j < 4) return rowbase + 256 * w + 16 * (lane & 15);
+    return lane < 32 ? rowbase + 1024 + 16 * (lane & 7) : 0x80000000u;
+  }
+  __device__ static int row_of(int w, int lane, int j) { return j < 4 ? 4 * j + (lane >> 4) : 4 * w + ((lane >> 3) & 3); }
+};
+
+// whole rows end to end, four waves per query: chunk c = 64 j + lane of wave w's
+// 4 x 72 chunks (rows 4w..4w+3); lanes past the 288th chunk read nothing
+template <>
+struct Pattern<5> {
+  static constexpr int kLoads = 5;
+  static constexpr int kQueriesPerWg = 1;
+  __device__ static uint32_t offset(int, int lane, int j, uint32_t rowbase) {
+    const int c = 64 * j + lane;
+    return c < 4 * kChunks ? rowbase + 16 * (c % kChunks) : 0x80000000u;
+  }
+  __device__ static int row_of(int w, int lane, int j) {
+    const int c = 64 * j + lane;
+    return 4 * w + (c < 4 * kChunks ? c / kChunks : 3);
+  }
+};
+
+// one query per wave; per step: load r < 16 is row r's first KiB (one row per
+// instruction), loads 16 and 17 the 128-byte rope lines of rows 8k + lane/8
+template <>
+struct Pattern<6> {
+  static constexpr int kLoads = kStep + 2;
+  static constexpr int kQueriesPerWg = 4;
+  __device__ static uint32_t offset(int, int lane, int j, uint32_t rowbase) {
+    return j < kStep ? rowbase + 16 * lane : rowbase + 1024 + 16 * (lane & 7);
+  }
+  __device__ static int row_of(int, int lane, int j) { return j < kStep ? j : 8 * (j - kStep) + (lane >> 3); }
 };
 
 template <int MODE, int DEPTH>
@@ -117,7 +168,7 @@ __global__ __launch_bounds__(256) void gather_probe_kernel(ProbeParams p) {
   auto issue = [&](int step, u32x4 (&buf)[P::kLoads]) {
 #pragma unroll
     for (int j = 0; j < P::kLoads; ++j) {
-      const int e = step * kStep + P::row_of(lane, j);
+      const int e = step * kStep + P::row_of(w, lane, j);
       const int32_t s = (step < nsteps && e < p.topk) ? sidx[qq][e] : -1;
       const bool valid = s >= 0 && s < p.n_rows;
       const uint32_t base = valid ? (uint32_t)s * kRowB : 0x80000000u;
@@ -154,7 +205,8 @@ void launch(const ProbeParams& p, hipStream_t s) {
 namespace dsa_host {
 
 int64_t gather_probe_out_words(int64_t n_q, int32_t mode) {
-  const int qw = (mode == 6 || mode % 3 == 0) ? 1 : 4;
+  // queries per workgroup: one in modes 0, 3, 6, 7, 8; four in the others
+  const int qw = (mode == 0 || mode == 3 || (mode >= 6 && mode <= 8)) ? 1 : 4;
   return (n_q + qw - 1) / qw * 4;
 }
 
@@ -169,6 +221,9 @@ hipError_t gather_probe_launch(const void* table, int32_t n_rows, const int32_t*
     case 4: launch<1, 3>(p, s); break;
     case 5: launch<2, 3>(p, s); break;
     case 6: launch<3, 2>(p, s); break;
+    case 7: launch<4, 2>(p, s); break;
+    case 8: launch<5, 2>(p, s); break;
+    case 9: launch<6, 2>(p, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

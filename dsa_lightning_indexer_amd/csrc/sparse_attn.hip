@@ -19,7 +19,12 @@
 //    P^T needs no data movement: the S^T accumulator layout (lane = head,
 //    registers = 4 consecutive keys) is exactly the B-operand layout of the
 //    16x16x16 MFMA.  With several splits per row the partial (max, sum, O) go
-//    to the workspace and sa_combine_kernel merges them.
+//    to the workspace and sa_combine_kernel merges them.  Used below 1024 rows
+//    (decode), where rows are split to fill the chip.
+//  * sa_mla1_kernel     the same arithmetic with one wave per query row (from
+//    1024 rows, no splits): the wave gathers whole latent rows, one load
+//    instruction per row, which the chip serves faster than four waves each
+//    fetching a slice of every row, and needs no partial-score exchange.
 #include "common.hpp"
 
 namespace {
@@ -350,6 +355,180 @@ __global__ __launch_bounds__(256, 3) void sa_mla4_kernel(SAParams p) {
   }
 }
 
+// One wave per query row; the four waves of a workgroup work on four rows
+// independently (no barriers).  Per 16-position step the wave gathers the 16
+// selected latent rows whole, in registers two steps ahead: one load
+// instruction per row for its first KiB (the 512 V columns: 64 lanes x 16
+// bytes of that row alone) and two for the 16 rope lines (eight rows per
+// instruction, eight lanes per 128-byte line).  The rows go to the wave's LDS
+// tile, which serves the K fragments of all 18 K steps of S^T = K_sel . Q^T and
+// the transposed V fragments of all 32 output tiles of O^T += V_sel^T . P^T.
+// The softmax is the same lazily rescaled base-2 online softmax as above, on
+// the wave's own S^T.  The output accumulators (16 heads x 512 columns) take a
+// quarter of the register file, so a SIMD runs one such wave; the row tiles
+// and index rows of four waves fill two thirds of the LDS.
+template <int DQK, int DV>
+__global__ __launch_bounds__(256, 1) void sa_mla1_kernel(SAParams p, int64_t rows) {
+  constexpr int KS = DQK / 32;               // K steps of Q.K (18)
+  constexpr int NDT = DV / 16;               // output tiles of 16 columns (32)
+  constexpr int ROWB = DQK * 2;              // bytes per latent row (1152)
+  constexpr int VB = DV * 2;                 // V bytes per row: one load instruction
+  constexpr int NRL = (ROWB - VB) / 128;     // rope lines per row (1)
+  static_assert(VB == 64 * 16 && NRL == 1 && KS % 2 == 0 && NDT % 8 == 0, "latent layout: 1 KiB of V + one rope line");
+  constexpr int NLD = kTile + 2;             // load instructions per step
+  // LDS row pitch 1168 bytes (292 dwords, 36 mod 64 banks): the 16-byte K
+  // fragment reads (one row per lane) and the transposed 8-byte V reads are
+  // conflict-free
+  constexpr int PITCH = ROWB + 16;
+  constexpr int NSI = kMaxTopk + 3 * kTile;  // fetches run up to two steps past the row
+  __shared__ __attribute__((aligned(16))) uint8_t tile[4][kTile * PITCH];
+  __shared__ __attribute__((aligned(16))) uint32_t sidx_all[4][NSI];
+
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id();
+  const int64_t gi = (int64_t)blockIdx.x * 4 + w;    // flattened (batch, query row)
+  if (gi >= rows) return;                              // (no barriers below)
+  const int g = lane >> 4, col = lane & 15;
+  const int b = (int)(gi / p.n_q);
+  uint32_t* sidx = sidx_all[w];
+  uint8_t* tw = tile[w];
+
+  // Q^T as the B operand: lane holds head `col`, columns 32 ks + 8 g .. + 7
+  bf16x8 qf[KS];
+  const __bf16* qrow = (const __bf16*)p.q + (gi * kH + col) * (int64_t)DQK;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_nontemporal_load((const bf16x8*)(qrow + 32 * ks + 8 * g));
+
+  // the index row as byte offsets (kInvalid outside [0, n_k) and past the row)
+  {
+    const int32_t* ir = p.idx + gi * (int64_t)p.topk;
+    for (int e = lane; e < p.topk + 3 * kTile; e += 64) {
+      const int32_t s = e < p.topk ? ir[e] : -1;
+      sidx[e] = (s >= 0 && s < p.n_k) ? (uint32_t)s * ROWB : kInvalid;
+    }
+  }
+
+  f32x4 o[NDT];
+#pragma unroll
+  for (int d = 0; d < NDT; ++d) o[d] = f32x4{};
+  constexpr float kLazy = 8.f;
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  const float sl2 = p.scale * 1.4426950408889634f;   // scale * log2(e)
+
+  const __amdgpu_buffer_rsrc_t kvr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>((const void*)((const __bf16*)p.kv + (int64_t)b * p.kv_bs)), (short)0,
+      (int)((int64_t)p.n_k * DQK * 2), 0x00020000);
+  const uint32_t lv = 16u * (uint32_t)lane;                          // V: chunk `lane` of a row
+  const int rrow = lane >> 3;                                        // rope: row 8 k + lane / 8
+  const uint32_t lr = (uint32_t)VB + 16u * (uint32_t)(lane & 7);     //       chunk lane % 8 of its line
+
+  // st[r] (r < 16): row r's V bytes; st[16 + k]: the rope lines of rows 8k..8k+7.
+  // An invalid position's offset plus a column offset stays past the buffer
+  // range and reads zeros without touching memory.
+  auto fetch = [&](int t, u32x4 (&st)[NLD], uint64_t& vm) {
+    const uint32_t* si = sidx + t * kTile;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 r4 = *(const u32x4*)(si + 4 * q);    // (same address in every lane)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[4 * q + i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kvr, r4[i] + lv, 0, 0));
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      st[kTile + k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kvr, si[8 * k + rrow] + lr, 0, 0));
+    vm = ballot(si[col] != kInvalid);
+  };
+  uint8_t* wv = tw + 16 * lane;
+  uint8_t* wr = tw + rrow * PITCH + lr;
+  auto put = [&](const u32x4 (&st)[NLD]) {
+#pragma unroll
+    for (int r = 0; r < kTile; ++r) *(u32x4*)(wv + r * PITCH) = st[r];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) *(u32x4*)(wr + 8 * k * PITCH) = st[kTile + k];
+  };
+  // K fragment of step ks: row `col`, columns 32 ks + 8 g ..; transposed V
+  // fragment of output tile dt: rows 4 g .. 4 g + 3, column 16 dt + col
+  const uint8_t* frow = tw + col * PITCH + 16 * g;
+  const uint8_t* rbase = tw + (4 * g + (col >> 2)) * PITCH + 8 * (col & 3);
+
+  auto step = [&](uint64_t vm) {
+    f32x4 a0 = f32x4{}, a1 = f32x4{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ks += 2) {
+      const bf16x8 k0 = *(const bf16x8*)(frow + 64 * ks);
+      const bf16x8 k1 = *(const bf16x8*)(frow + 64 * (ks + 1));
+      a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[ks], a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[ks + 1], a1, 0, 0, 0);
+    }
+    const f32x4 sc = a0 + a1;
+    // sc[i]: head `col`, position 4 g + i of this step
+    const uint32_t vb = (uint32_t)(vm >> (4 * g));
+    float z[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z[i] = ((vb >> i) & 1u) ? sc[i] * sl2 : -__builtin_inff();
+    const float mx = quad_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+    const bool bump = mx > m_run + kLazy;
+    if (ballot(bump)) {
+      const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+      m_run = bump ? mx : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+    }
+    const float mref = fmaxf(m_run, -__FLT_MAX__);
+    float pe[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pe[i] = __builtin_amdgcn_exp2f(z[i] - mref);
+    bf16x4 pb_hi, pb_lo;
+    split_bf16(pe, pb_hi, pb_lo);
+    l_run += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+    // eight output tiles at a time, so that the hi and lo products of one tile
+    // are eight MFMAs apart
+#pragma unroll
+    for (int d0 = 0; d0 < NDT; d0 += 8) {
+      bf16x4 va[8];
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+        va[d] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(rbase + 32 * (d0 + d)));
+#pragma unroll
+      for (int d = 0; d < 8; ++d) o[d0 + d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[d], pb_hi, o[d0 + d], 0, 0, 0);
+#pragma unroll
+      for (int d = 0; d < 8; ++d) o[d0 + d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[d], pb_lo, o[d0 + d], 0, 0, 0);
+    }
+    // the tile is rewritten next step only after these reads returned
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  };
+
+  // two register buffers: a step's rows go to the tile, then the same registers
+  // take the gathers two steps ahead while the tile is consumed
+  const int nst = (p.topk + kTile - 1) / kTile;
+  u32x4 stA[NLD], stB[NLD];
+  uint64_t vmA = 0, vmB = 0;
+  fetch(0, stA, vmA);
+  fetch(1, stB, vmB);
+  int t = 0;
+  for (; t + 1 < nst; t += 2) {
+    put(stA);
+    uint64_t vm = vmA;
+    fetch(t + 2, stA, vmA);
+    step(vm);
+    put(stB);
+    vm = vmB;
+    fetch(t + 3, stB, vmB);
+    step(vm);
+  }
+  if (t < nst) {            // odd step count: the last step
+    put(stA);
+    step(vmA);
+  }
+  l_run = quad_sum(l_run);
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  // O^T layout: lane holds head `col`, columns 16 dt + 4 g + (0..3)
+  float* out = p.out + (gi * kH + col) * (int64_t)DV + 4 * g;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) __builtin_nontemporal_store(o[dt] * inv, (f32x4*)(out + 16 * dt));
+}
+
 // Merge the split partials of one (query row, head): thread c loads column c of
 // every split's partial output first (all loads in flight at once), while wave
 // 0 forms the weights exp(m_s - M) in LDS; then each thread sums its column.
@@ -389,8 +568,13 @@ bool mla_ok(const dsa_sparse_attn_args& a) {
          a.d_v == 512 && a.v == nullptr && (int64_t)a.n_k * a.d_qk * 2 < ((int64_t)1 << 31);
 }
 
+// Row counts from which the one-wave-per-row kernel runs (one split per row):
+// at 1024 rows its 256 workgroups give every CU one.
+constexpr int64_t kWaveRows = 1024;
+
 int pick_nsplit(const dsa_sparse_attn_args& a) {
   const int64_t rows = (int64_t)a.batch * a.n_q;
+  if (rows >= kWaveRows) return 1;
   int64_t ns = (1024 + rows - 1) / rows;
   int64_t maxs = a.topk / 64;
   if (maxs < 1) maxs = 1;
@@ -428,6 +612,10 @@ hipError_t sparse_attn_launch(const dsa_sparse_attn_args& a, void* ws, hipStream
   if (mla_ok(a)) {
     p.nsplit = pick_nsplit(a);
     const int64_t rows = (int64_t)a.batch * a.n_q;
+    if (rows >= kWaveRows) {
+      hipLaunchKernelGGL((sa_mla1_kernel<576, 512>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, rows);
+      return hipGetLastError();
+    }
     if (p.nsplit > 1) {
       p.ws_o = (float*)ws;
       p.ws_ml = p.ws_o + rows * p.nsplit * a.heads * (int64_t)a.d_v;

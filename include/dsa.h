@@ -365,6 +365,14 @@ dsa_status dsa_pattern_search(const double* S, int32_t n_layers, int32_t n_full,
  *           6: four waves per query reading as the attention kernel does: a
  *              wave's 256-byte V slice of four rows per load (whole lines),
  *              then the 64-byte rope slice of 16 rows (two steps in flight)
+ *           7: mode 6 with the rope line split by rows: wave w reads the whole
+ *              128-byte rope line of rows 4w..4w+3
+ *           8: four waves per query, wave w reading rows 4w..4w+3 of each step
+ *              whole, end to end (mode 2's pattern split over four waves)
+ *           9: one wave per query reading as the one-wave-per-row attention
+ *              kernel does: one load instruction per selected row for its first
+ *              KiB, two for the 16 rope lines (eight rows each), two steps in
+ *              flight
  *   out     device uint32 [dsa_gather_probe_out_words(n_q, mode)] checksums
  */
 int64_t dsa_gather_probe_out_words(int64_t n_q, int32_t mode);

@@ -65,14 +65,20 @@ def test_mla_decode_split(dsa, dev):
     check_sa(dsa, sa, idx)
 
 
-def test_mla_invalid_entries_and_empty_rows(dsa, dev):
-    n = 300
+@pytest.mark.parametrize("n", [300, 1103])
+def test_mla_invalid_entries_and_empty_rows(dsa, dev, n):
+    """Empty rows, out-of-range entries and ragged row counts.  300 rows run the
+    four-waves-per-row kernel with split index rows; 1103 rows the
+    one-wave-per-row kernel (from 1024 rows), whose last workgroup has three
+    rows."""
     sa = syn.sa_inputs(n_q=n, n_k=n, seed=7, device=dev)
     idx = syn.random_sorted_indices(n_q=n, topk=2048, seed=8, device=dev)
     idx[0, 10] = -1                      # an empty row -> zeros
     idx[0, 11, :] = n + 5                # out of range -> selects nothing
     idx[0, 12, 5] = 10 ** 9              # one bad entry among valid ones
-    got = check_sa(dsa, sa, idx, np.arange(0, 40))
+    idx[0, n - 2, 100:] = -1             # a row that ends early
+    rows = np.concatenate([np.arange(0, 40), np.arange(n - 5, n)])
+    got = check_sa(dsa, sa, idx, rows)
     assert (got[0, 10] == 0).all() and (got[0, 11] == 0).all()
 
 
@@ -109,7 +115,7 @@ def test_overlap_counts(dsa, dev):
     assert ov == pytest.approx(oracle.overlap(an, bn, k, rows))
 
 
-@pytest.mark.parametrize("mode", range(7))
+@pytest.mark.parametrize("mode", range(10))
 def test_gather_probe_reads_every_selected_row(dsa, dev, mode):
     """The gather probe (measurement helper) reads each valid selected 1152-byte
     row exactly once per query: the XOR of its per-wave checksums equals the XOR
@@ -132,7 +138,7 @@ def test_gather_probe_reads_every_selected_row(dsa, dev, mode):
     for q in range(n_q):
         sel = ix[q][(ix[q] >= 0) & (ix[q] < n_rows)]
         want = np.bitwise_xor.reduce(words[sel].ravel()) if sel.size else np.uint32(0)
-        have = np.bitwise_xor.reduce(got[4 * q:4 * q + 4]) if (mode == 6 or mode % 3 == 0) else got[q]
+        have = np.bitwise_xor.reduce(got[4 * q:4 * q + 4]) if mode in (0, 3, 6, 7, 8) else got[q]
         assert have == want, (mode, q)
 
 
