@@ -178,7 +178,8 @@ PROBE_MODES = {0: "quarter rows, 2 steps in flight (the attention kernel's patte
                6: "the attention kernel's pattern: 256-B V slices of 4 rows per load + rope, 2 steps",
                7: "mode 6 with each rope line read whole by one wave (rows 4w..4w+3)",
                8: "four waves per query, wave w reads rows 4w..4w+3 whole, end to end",
-               9: "the one-wave-per-query attention pattern: one instruction per row's V KiB + 2 rope-line loads, 2 steps"}
+               9: "the one-wave-per-query attention pattern: one instruction per row's V KiB + 2 rope-line loads, 2 steps",
+               10: "mode 9's instructions landing in LDS by DMA, with the DMA attention kernel's two tiles per wave and index ring"}
 
 
 def gather_ceiling(dsa, kv, idx, reps):

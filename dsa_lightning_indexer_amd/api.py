@@ -259,7 +259,7 @@ def pattern_search(S, n_full):
 def gather_probe(kv, idx, mode, *, out=None):
     """Measurement helper: read every selected 1152-byte latent row (kv
     [n_rows, 576] bf16 or [n_rows, 1, 576]) of idx [n_q, topk] with access
-    pattern `mode` (0..9); returns the uint32 checksums (as int32)."""
+    pattern `mode` (0..10); returns the uint32 checksums (as int32)."""
     n_rows = kv.shape[0]
     L._dense("kv", kv)
     L._dense("idx", idx)

@@ -629,14 +629,14 @@ dsa_status dsa_similarity_matrix(int32_t n, const dsa_layer* layers, int32_t k, 
 }
 
 int64_t dsa_gather_probe_out_words(int64_t n_q, int32_t mode) {
-  if (n_q < 1 || mode < 0 || mode > 9) return 0;
+  if (n_q < 1 || mode < 0 || mode > 10) return 0;
   return dsa_host::gather_probe_out_words(n_q, mode);
 }
 
 dsa_status dsa_gather_probe(const void* table, int32_t n_rows, const int32_t* idx, int64_t n_q, int32_t topk,
                             int32_t mode, uint32_t* out, hipStream_t stream) {
   g_last_error.clear();
-  if (mode < 0 || mode > 9) return fail(DSA_ERR_INVALID, "mode must be 0..9");
+  if (mode < 0 || mode > 10) return fail(DSA_ERR_INVALID, "mode must be 0..10");
   if (n_rows < 1 || (int64_t)n_rows * 1152 >= ((int64_t)1 << 31))
     return fail(DSA_ERR_UNSUPPORTED, "n_rows must be 1..%lld (1152-byte rows, 32-bit offsets)",
                 (long long)((((int64_t)1 << 31) - 1) / 1152));

@@ -31,6 +31,10 @@
 //           wave; per step one load instruction per row for its first KiB (64
 //           lanes, that row alone) and two for the 16 rope lines (eight rows
 //           per instruction, eight lanes per line), two steps in flight
+//   mode 10 the same instructions landing in LDS (buffer_load ... lds) with the
+//           DMA attention kernel's schedule: two row tiles per wave (one being
+//           read, one being filled), the index row through a four-block ring,
+//           each step's tile read back whole once
 #include "common.hpp"
 
 namespace {
@@ -200,6 +204,82 @@ void launch(const ProbeParams& p, hipStream_t s) {
   hipLaunchKernelGGL((gather_probe_kernel<MODE, DEPTH>), dim3((unsigned)wgs), dim3(256), 0, s, p);
 }
 
+// mode 10: the schedule of the DMA attention kernel without its arithmetic
+constexpr int kDmaVP = 1040;                       // V row pitch in a tile
+constexpr int kDmaRope = kStep * kDmaVP;           // rope lines after the V rows
+constexpr int kDmaTB = kDmaRope + kStep * 128;     // tile bytes
+__global__ __launch_bounds__(256, 1) void gather_dma_kernel(ProbeParams p) {
+  constexpr int NRING = 4;
+  constexpr uint32_t kInv = 0x80000000u;
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[4][2][kDmaTB];
+  __shared__ __attribute__((aligned(16))) uint32_t ring_all[4][NRING][64];
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id();
+  const int64_t q = (int64_t)blockIdx.x * 4 + w;
+  if (q >= p.n_q) return;                          // (no barriers below)
+  uint32_t (*ring)[64] = ring_all[w];
+  const int topk = p.topk;
+  const __amdgpu_buffer_rsrc_t kvr = make_rsrc(p.table, p.table_bytes);
+  const __amdgpu_buffer_rsrc_t irs = make_rsrc(p.idx + q * topk, (uint32_t)topk * 4u);
+  const int nst = (topk + kStep - 1) / kStep;
+  const int nblk = (topk + 63) / 64;
+  auto idx_dma = [&](int m) { lds_dma<4>(irs, (const uint8_t*)ring[m % NRING], (uint32_t)(64 * m + lane) * 4u); };
+  auto idx_conv = [&](int m) {
+    uint32_t* sl = ring[m % NRING];
+    const int e = 64 * m + lane;
+    const int32_t s = (int32_t)sl[lane];
+    sl[lane] = (e < topk && s >= 0 && s < p.n_rows) ? (uint32_t)s * kRowB : kInv;
+  };
+  const uint32_t lv = 16u * (uint32_t)lane;
+  const int rj = lane >> 3;
+  const uint32_t lr0 = 1024u + 16u * (uint32_t)((lane - rj) & 7);
+  const uint32_t lr1 = 1024u + 16u * (uint32_t)((lane - rj - 1) & 7);
+  auto row_dma = [&](int t, uint8_t* dst) {
+    const uint32_t dead = t < nst ? 0u : kInv;
+    const uint32_t* si = ring[(t >> 2) % NRING] + 16 * (t & 3);
+    u32x4 r4[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) r4[qq] = *(const u32x4*)(si + 4 * qq);
+    const uint32_t o0 = si[rj] | dead, o1 = si[8 + rj] | dead;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lds_dma<16>(kvr, dst + (4 * qq + i) * kDmaVP, (r4[qq][i] | dead) + lv);
+    lds_dma<16>(kvr, dst + kDmaRope, o0 + lr0);
+    lds_dma<16>(kvr, dst + kDmaRope + 1024, o1 + lr1);
+  };
+  uint32_t acc = 0;
+  auto consume = [&](const uint8_t* tile) {
+#pragma unroll
+    for (int r = 0; r < kStep; ++r) acc ^= xor4(*(const u32x4*)(tile + r * kDmaVP + 16 * lane));
+#pragma unroll
+    for (int k = 0; k < 2; ++k) acc ^= xor4(*(const u32x4*)(tile + kDmaRope + 1024 * k + 16 * lane));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+  idx_dma(0);
+  if (nblk > 1) idx_dma(1);
+  vm_wait<0>();
+  idx_conv(0);
+  row_dma(0, tiles[w][0]);
+  row_dma(1, tiles[w][1]);
+  for (int t = 0; t < nst; t += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int tt = t + h;
+      if (h == 1 && tt >= nst) break;
+      vm_wait<kStep + 2>();
+      if ((tt & 3) == 0 && (tt >> 2) + 1 < nblk) idx_conv((tt >> 2) + 1);
+      consume(tiles[w][h]);
+      if ((tt & 3) == 0 && (tt >> 2) + 2 < nblk) idx_dma((tt >> 2) + 2);
+      row_dma(tt + 2, tiles[w][h]);
+    }
+  }
+  vm_wait<0>();
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o, 64);
+  if (lane == 0) p.out[(int64_t)blockIdx.x * 4 + w] = acc;
+}
+
 }  // namespace
 
 namespace dsa_host {
@@ -224,6 +304,7 @@ hipError_t gather_probe_launch(const void* table, int32_t n_rows, const int32_t*
     case 7: launch<4, 2>(p, s); break;
     case 8: launch<5, 2>(p, s); break;
     case 9: launch<6, 2>(p, s); break;
+    case 10: hipLaunchKernelGGL(gather_dma_kernel, dim3((unsigned)((p.n_q + 3) / 4)), dim3(256), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -340,34 +340,6 @@ __device__ __forceinline__ void store_ktile(uint8_t* dst, const i32x4 (&pre)[Cfg
   }
 }
 
-// Buffer-resource view of a byte range (gfx9 family resource word: raw buffer,
-// out-of-range reads return zero).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-
-// One buffer_load ... lds of `bytes` (4 or 16) per lane at byte offset voff,
-// landing at LDS address lds + bytes * lane.  Issued from inline asm so that
-// the compiler's wait-count tracking, which would otherwise wait for the load
-// before every later LDS read of the same array, leaves it alone; callers wait
-// for it explicitly (vmcnt) before the barrier that publishes the data.  The
-// load takes its LDS base from M0, which the compiler reserves: the asm saves
-// M0, sets it (one wait state before the load reads it) and restores it.  Its
-// only register output is that saved copy.
-template <int BYTES>
-__device__ __forceinline__ void lds_dma(__amdgpu_buffer_rsrc_t r, const uint8_t* lds, uint32_t voff) {
-  const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)lds;
-  uint32_t saved;
-  if constexpr (BYTES == 16)
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-                 "s_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(a), "v"(voff), "s"(r) : "memory");
-  else
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %2, %3, 0 offen lds\n\t"
-                 "s_mov_b32 m0, %0"
-                 : "=&s"(saved) : "s"(a), "v"(voff), "s"(r) : "memory");
-}
 
 // Workgroup barrier without the fence of __syncthreads (whose release would
 // wait for every load in flight, including the next tiles' staging): LDS

@@ -22,9 +22,10 @@
 //    to the workspace and sa_combine_kernel merges them.  Used below 1024 rows
 //    (decode), where rows are split to fill the chip.
 //  * sa_mla1_kernel     the same arithmetic with one wave per query row (from
-//    1024 rows, no splits): the wave gathers whole latent rows, one load
-//    instruction per row, which the chip serves faster than four waves each
-//    fetching a slice of every row, and needs no partial-score exchange.
+//    1024 rows, no splits): the wave gathers whole latent rows straight into
+//    LDS, one load instruction per row, which the chip serves faster than four
+//    waves each fetching a slice of every row into registers, and needs no
+//    partial-score exchange.
 #include "common.hpp"
 
 namespace {
@@ -357,32 +358,41 @@ __global__ __launch_bounds__(256, 3) void sa_mla4_kernel(SAParams p) {
 
 // One wave per query row; the four waves of a workgroup work on four rows
 // independently (no barriers).  Per 16-position step the wave gathers the 16
-// selected latent rows whole, in registers two steps ahead: one load
+// selected latent rows whole, straight into LDS (buffer_load ... lds): one load
 // instruction per row for its first KiB (the 512 V columns: 64 lanes x 16
 // bytes of that row alone) and two for the 16 rope lines (eight rows per
-// instruction, eight lanes per 128-byte line).  The rows go to the wave's LDS
-// tile, which serves the K fragments of all 18 K steps of S^T = K_sel . Q^T and
-// the transposed V fragments of all 32 output tiles of O^T += V_sel^T . P^T.
-// The softmax is the same lazily rescaled base-2 online softmax as above, on
-// the wave's own S^T.  The output accumulators (16 heads x 512 columns) take a
-// quarter of the register file, so a SIMD runs one such wave; the row tiles
-// and index rows of four waves fill two thirds of the LDS.
+// instruction, eight lanes per 128-byte line).  Each wave has two row tiles,
+// the one being consumed and the one being filled two steps ahead.  A tile
+// holds the V bytes at a 1040-byte row pitch (260 dwords = 4 mod 64 banks, so
+// the row-per-lane K-fragment reads and the transposed V reads are
+// conflict-free) and, after them, the rope lines: rope load k (rows 8k..8k+7)
+// puts chunk c of row 8k + j in slot 64k + 8j + ((c + j + k) mod 8), which
+// spreads the 16 rows' reads of one chunk over 16 distinct bank groups.  The
+// tile serves all 18 K steps of S^T = K_sel . Q^T and all 32 output tiles of
+// O^T += V_sel^T . P^T, so there is no partial-score exchange and the softmax
+// (the same lazily rescaled base-2 online softmax as above) runs once per row.
+// The index row goes through a per-wave ring of four 64-entry blocks, also by
+// DMA (an LDS copy of the whole row would not fit beside the tiles), converted
+// to byte offsets in place.  The output accumulators (16 heads x 512 columns)
+// and Q^T take the register file of one wave per SIMD.  The DMAs are invisible to the
+// compiler's wait counting: every wait on them is explicit, and a tile is
+// refilled only after every read of the step that consumed it returned.
 template <int DQK, int DV>
 __global__ __launch_bounds__(256, 1) void sa_mla1_kernel(SAParams p, int64_t rows) {
   constexpr int KS = DQK / 32;               // K steps of Q.K (18)
+  constexpr int KSV = DV / 32;               // K steps inside V (16)
   constexpr int NDT = DV / 16;               // output tiles of 16 columns (32)
   constexpr int ROWB = DQK * 2;              // bytes per latent row (1152)
   constexpr int VB = DV * 2;                 // V bytes per row: one load instruction
-  constexpr int NRL = (ROWB - VB) / 128;     // rope lines per row (1)
-  static_assert(VB == 64 * 16 && NRL == 1 && KS % 2 == 0 && NDT % 8 == 0, "latent layout: 1 KiB of V + one rope line");
-  constexpr int NLD = kTile + 2;             // load instructions per step
-  // LDS row pitch 1168 bytes (292 dwords, 36 mod 64 banks): the 16-byte K
-  // fragment reads (one row per lane) and the transposed 8-byte V reads are
-  // conflict-free
-  constexpr int PITCH = ROWB + 16;
-  constexpr int NSI = kMaxTopk + 3 * kTile;  // fetches run up to two steps past the row
-  __shared__ __attribute__((aligned(16))) uint8_t tile[4][kTile * PITCH];
-  __shared__ __attribute__((aligned(16))) uint32_t sidx_all[4][NSI];
+  static_assert(VB == 64 * 16 && ROWB - VB == 128 && KS == KSV + 2 && NDT % 8 == 0,
+                "latent layout: 1 KiB of V + one rope line");
+  constexpr int VP = VB + 16;                // V row pitch (1040)
+  constexpr int ROPE = kTile * VP;           // rope slots start (16640)
+  constexpr int TB = ROPE + kTile * 128;     // tile bytes (18688)
+  constexpr int NLD = kTile + 2;             // row loads per step
+  constexpr int NRING = 4;                   // index blocks of 64 entries
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[4][2][TB];
+  __shared__ __attribute__((aligned(16))) uint32_t ring_all[4][NRING][64];
 
   const int lane = threadIdx.x & 63;
   const int w = wave_id();
@@ -390,23 +400,13 @@ __global__ __launch_bounds__(256, 1) void sa_mla1_kernel(SAParams p, int64_t row
   if (gi >= rows) return;                              // (no barriers below)
   const int g = lane >> 4, col = lane & 15;
   const int b = (int)(gi / p.n_q);
-  uint32_t* sidx = sidx_all[w];
-  uint8_t* tw = tile[w];
+  uint32_t (*ring)[64] = ring_all[w];
+  const int topk = p.topk;
 
-  // Q^T as the B operand: lane holds head `col`, columns 32 ks + 8 g .. + 7
   bf16x8 qf[KS];
   const __bf16* qrow = (const __bf16*)p.q + (gi * kH + col) * (int64_t)DQK;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_nontemporal_load((const bf16x8*)(qrow + 32 * ks + 8 * g));
-
-  // the index row as byte offsets (kInvalid outside [0, n_k) and past the row)
-  {
-    const int32_t* ir = p.idx + gi * (int64_t)p.topk;
-    for (int e = lane; e < p.topk + 3 * kTile; e += 64) {
-      const int32_t s = e < p.topk ? ir[e] : -1;
-      sidx[e] = (s >= 0 && s < p.n_k) ? (uint32_t)s * ROWB : kInvalid;
-    }
-  }
 
   f32x4 o[NDT];
 #pragma unroll
@@ -415,53 +415,71 @@ __global__ __launch_bounds__(256, 1) void sa_mla1_kernel(SAParams p, int64_t row
   float m_run = -__builtin_inff(), l_run = 0.f;
   const float sl2 = p.scale * 1.4426950408889634f;   // scale * log2(e)
 
-  const __amdgpu_buffer_rsrc_t kvr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void*>((const void*)((const __bf16*)p.kv + (int64_t)b * p.kv_bs)), (short)0,
-      (int)((int64_t)p.n_k * DQK * 2), 0x00020000);
-  const uint32_t lv = 16u * (uint32_t)lane;                          // V: chunk `lane` of a row
-  const int rrow = lane >> 3;                                        // rope: row 8 k + lane / 8
-  const uint32_t lr = (uint32_t)VB + 16u * (uint32_t)(lane & 7);     //       chunk lane % 8 of its line
+  const __amdgpu_buffer_rsrc_t kvr =
+      make_rsrc((const __bf16*)p.kv + (int64_t)b * p.kv_bs, (uint32_t)((int64_t)p.n_k * ROWB));
+  // the index row (entries past it read zero and are marked invalid below)
+  const __amdgpu_buffer_rsrc_t irs = make_rsrc(p.idx + gi * (int64_t)topk, (uint32_t)topk * 4u);
+  const int nst = (topk + kTile - 1) / kTile;
+  const int nblk = (topk + 63) / 64;
 
-  // st[r] (r < 16): row r's V bytes; st[16 + k]: the rope lines of rows 8k..8k+7.
-  // An invalid position's offset plus a column offset stays past the buffer
-  // range and reads zeros without touching memory.
-  auto fetch = [&](int t, u32x4 (&st)[NLD], uint64_t& vm) {
-    const uint32_t* si = sidx + t * kTile;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const u32x4 r4 = *(const u32x4*)(si + 4 * q);    // (same address in every lane)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st[4 * q + i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kvr, r4[i] + lv, 0, 0));
-    }
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-      st[kTile + k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kvr, si[8 * k + rrow] + lr, 0, 0));
-    vm = ballot(si[col] != kInvalid);
+  auto idx_dma = [&](int m) { lds_dma<4>(irs, (const uint8_t*)ring[m % NRING], (uint32_t)(64 * m + lane) * 4u); };
+  auto idx_conv = [&](int m) {
+    uint32_t* sl = ring[m % NRING];
+    const int e = 64 * m + lane;
+    const int32_t s = (int32_t)sl[lane];
+    sl[lane] = (e < topk && s >= 0 && s < p.n_k) ? (uint32_t)s * ROWB : kInvalid;
   };
-  uint8_t* wv = tw + 16 * lane;
-  uint8_t* wr = tw + rrow * PITCH + lr;
-  auto put = [&](const u32x4 (&st)[NLD]) {
+  const uint32_t lv = 16u * (uint32_t)lane;
+  const int rj = lane >> 3;                                        // rope: row 8k + rj
+  // rope: chunk (lane - rj - k) mod 8 of the line, for loads k = 0, 1
+  const uint32_t lr0 = (uint32_t)VB + 16u * (uint32_t)((lane - rj) & 7);
+  const uint32_t lr1 = (uint32_t)VB + 16u * (uint32_t)((lane - rj - 1) & 7);
+  // row DMA of step t into tile `dst` (kInvalid offsets past the last step)
+  // (the ring slot is read in any case; past the last step every offset gets the
+  // kInvalid bit, so no branch is needed)
+  auto row_dma = [&](int t, uint8_t* dst, uint64_t& vm) {
+    const uint32_t dead = t < nst ? 0u : kInvalid;
+    const uint32_t* si = ring[(t >> 2) % NRING] + 16 * (t & 3);
+    u32x4 r4[4];
 #pragma unroll
-    for (int r = 0; r < kTile; ++r) *(u32x4*)(wv + r * PITCH) = st[r];
+    for (int q = 0; q < 4; ++q) r4[q] = *(const u32x4*)(si + 4 * q);
+    const uint32_t o0 = si[rj] | dead, o1 = si[8 + rj] | dead, oc = si[col] | dead;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) *(u32x4*)(wr + 8 * k * PITCH) = st[kTile + k];
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lds_dma<16>(kvr, dst + (4 * q + i) * VP, (r4[q][i] | dead) + lv);
+    lds_dma<16>(kvr, dst + ROPE, o0 + lr0);
+    lds_dma<16>(kvr, dst + ROPE + 1024, o1 + lr1);
+    vm = ballot(oc != kInvalid);
   };
-  // K fragment of step ks: row `col`, columns 32 ks + 8 g ..; transposed V
-  // fragment of output tile dt: rows 4 g .. 4 g + 3, column 16 dt + col
-  const uint8_t* frow = tw + col * PITCH + 16 * g;
-  const uint8_t* rbase = tw + (4 * g + (col >> 2)) * PITCH + 8 * (col & 3);
+  // K fragments: V steps at row `col` of the V area; rope steps ks' = 0, 1 read
+  // chunk 4 ks' + g of row `col` from its slot
+  const int rk = col >> 3, rr = col & 7;
+  const uint32_t fv = (uint32_t)(col * VP + 16 * g);
+  const uint32_t fr0 = (uint32_t)(ROPE + 16 * (64 * rk + 8 * rr + ((g + rr + rk) & 7)));
+  const uint32_t fr1 = (uint32_t)(ROPE + 16 * (64 * rk + 8 * rr + ((4 + g + rr + rk) & 7)));
+  const uint32_t fvt = (uint32_t)((4 * g + (col >> 2)) * VP + 8 * (col & 3));
 
-  auto step = [&](uint64_t vm) {
+  // Consume the tile of one step; `refill` is called once every read of the
+  // tile has returned.  (Refilling earlier -- before the P.V products, or as
+  // soon as all fragments are in registers -- measured slower: 25.1 and 29.4 ms
+  // against 24.5 ms on the C4 layer.)
+  auto step = [&](const uint8_t* tile, uint64_t vm, auto&& refill) {
     f32x4 a0 = f32x4{}, a1 = f32x4{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ks += 2) {
-      const bf16x8 k0 = *(const bf16x8*)(frow + 64 * ks);
-      const bf16x8 k1 = *(const bf16x8*)(frow + 64 * (ks + 1));
+    for (int ks = 0; ks < KSV; ks += 2) {
+      const bf16x8 k0 = *(const bf16x8*)(tile + fv + 64 * ks);
+      const bf16x8 k1 = *(const bf16x8*)(tile + fv + 64 * (ks + 1));
       a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[ks], a0, 0, 0, 0);
       a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[ks + 1], a1, 0, 0, 0);
     }
+    {
+      const bf16x8 k0 = *(const bf16x8*)(tile + fr0);
+      const bf16x8 k1 = *(const bf16x8*)(tile + fr1);
+      a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[KSV], a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[KSV + 1], a1, 0, 0, 0);
+    }
     const f32x4 sc = a0 + a1;
-    // sc[i]: head `col`, position 4 g + i of this step
     const uint32_t vb = (uint32_t)(vm >> (4 * g));
     float z[4];
 #pragma unroll
@@ -482,48 +500,51 @@ __global__ __launch_bounds__(256, 1) void sa_mla1_kernel(SAParams p, int64_t row
     bf16x4 pb_hi, pb_lo;
     split_bf16(pe, pb_hi, pb_lo);
     l_run += (pe[0] + pe[1]) + (pe[2] + pe[3]);
-    // eight output tiles at a time, so that the hi and lo products of one tile
-    // are eight MFMAs apart
 #pragma unroll
     for (int d0 = 0; d0 < NDT; d0 += 8) {
       bf16x4 va[8];
 #pragma unroll
       for (int d = 0; d < 8; ++d)
-        va[d] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(rbase + 32 * (d0 + d)));
+        va[d] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tile + fvt + 32 * (d0 + d)));
 #pragma unroll
       for (int d = 0; d < 8; ++d) o[d0 + d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[d], pb_hi, o[d0 + d], 0, 0, 0);
 #pragma unroll
       for (int d = 0; d < 8; ++d) o[d0 + d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[d], pb_lo, o[d0 + d], 0, 0, 0);
     }
-    // the tile is rewritten next step only after these reads returned
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    refill();
   };
 
-  // two register buffers: a step's rows go to the tile, then the same registers
-  // take the gathers two steps ahead while the tile is consumed
-  const int nst = (p.topk + kTile - 1) / kTile;
-  u32x4 stA[NLD], stB[NLD];
+  idx_dma(0);
+  if (nblk > 1) idx_dma(1);
+  vm_wait<0>();
+  idx_conv(0);                 // (block 1 is converted at the top of step 0)
   uint64_t vmA = 0, vmB = 0;
-  fetch(0, stA, vmA);
-  fetch(1, stB, vmB);
-  int t = 0;
-  for (; t + 1 < nst; t += 2) {
-    put(stA);
-    uint64_t vm = vmA;
-    fetch(t + 2, stA, vmA);
-    step(vm);
-    put(stB);
-    vm = vmB;
-    fetch(t + 3, stB, vmB);
-    step(vm);
+  row_dma(0, tiles[w][0], vmA);
+  row_dma(1, tiles[w][1], vmB);
+  // Per step t: wait for its rows (the next step's NLD loads stay in flight),
+  // consume them, then refill the tile with step t + 2 (preceded, every fourth
+  // step, by the index block two blocks ahead).  Index block m + 1 is converted
+  // at the top of step 4m: its DMA, issued at step 4m - 4, is older than the
+  // rows waited for there.
+  for (int t = 0; t < nst; t += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int tt = t + h;
+      if (h == 1 && tt >= nst) break;
+      vm_wait<NLD>();
+      if ((tt & 3) == 0 && (tt >> 2) + 1 < nblk) idx_conv((tt >> 2) + 1);
+      uint64_t& vmr = h == 0 ? vmA : vmB;
+      const uint64_t vm = vmr;
+      step(tiles[w][h], vm, [&] {
+        if ((tt & 3) == 0 && (tt >> 2) + 2 < nblk) idx_dma((tt >> 2) + 2);
+        row_dma(tt + 2, tiles[w][h], vmr);
+      });
+    }
   }
-  if (t < nst) {            // odd step count: the last step
-    put(stA);
-    step(vmA);
-  }
+  vm_wait<0>();
   l_run = quad_sum(l_run);
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  // O^T layout: lane holds head `col`, columns 16 dt + 4 g + (0..3)
   float* out = p.out + (gi * kH + col) * (int64_t)DV + 4 * g;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) __builtin_nontemporal_store(o[dt] * inv, (f32x4*)(out + 16 * dt));

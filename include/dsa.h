@@ -373,6 +373,9 @@ dsa_status dsa_pattern_search(const double* S, int32_t n_layers, int32_t n_full,
  *              kernel does: one load instruction per selected row for its first
  *              KiB, two for the 16 rope lines (eight rows each), two steps in
  *              flight
+ *           10: mode 9's load instructions landing in LDS (buffer_load ... lds)
+ *              with the prefill attention kernel's schedule: two row tiles per
+ *              wave, the index row through a four-block LDS ring
  *   out     device uint32 [dsa_gather_probe_out_words(n_q, mode)] checksums
  */
 int64_t dsa_gather_probe_out_words(int64_t n_q, int32_t mode);

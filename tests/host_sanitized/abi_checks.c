@@ -123,10 +123,10 @@ static void check_helpers(void) {
   EXPECT(dsa_index_overlap((const int32_t*)FAKE, (const int32_t*)FAKE, 4, 0, (int32_t*)FAKE, NULL, NULL) ==
          DSA_ERR_INVALID);
   EXPECT(dsa_row_cosine((const float*)FAKE, (const float*)FAKE, 4, 6, (float*)FAKE, NULL, NULL) == DSA_ERR_INVALID);
-  EXPECT(dsa_gather_probe(FAKE, 100, (const int32_t*)FAKE, 4, 16, 10, (uint32_t*)FAKE, NULL) == DSA_ERR_INVALID);
+  EXPECT(dsa_gather_probe(FAKE, 100, (const int32_t*)FAKE, 4, 16, 11, (uint32_t*)FAKE, NULL) == DSA_ERR_INVALID);
   EXPECT(dsa_gather_probe_out_words(5, 1) == 8 && dsa_gather_probe_out_words(5, 0) == 20 &&
          dsa_gather_probe_out_words(5, 6) == 20 &&
-         dsa_gather_probe_out_words(5, 7) == 20 && dsa_gather_probe_out_words(5, 8) == 20 && dsa_gather_probe_out_words(5, 9) == 8 && dsa_gather_probe_out_words(5, 10) == 0);
+         dsa_gather_probe_out_words(5, 7) == 20 && dsa_gather_probe_out_words(5, 8) == 20 && dsa_gather_probe_out_words(5, 9) == 8 && dsa_gather_probe_out_words(5, 10) == 8 && dsa_gather_probe_out_words(5, 11) == 0);
   EXPECT(dsa_stream_probe(FAKE, 16384 * 3 + 4, 8, 2, (uint32_t*)FAKE, NULL) == DSA_ERR_INVALID);
   EXPECT(dsa_stream_probe(FAKE, 16384, 8, 3, (uint32_t*)FAKE, NULL) == DSA_ERR_INVALID);
   EXPECT(dsa_stream_probe(FAKE, (int64_t)1 << 31, 8, 2, (uint32_t*)FAKE, NULL) == DSA_ERR_INVALID);

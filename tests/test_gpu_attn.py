@@ -115,7 +115,7 @@ def test_overlap_counts(dsa, dev):
     assert ov == pytest.approx(oracle.overlap(an, bn, k, rows))
 
 
-@pytest.mark.parametrize("mode", range(10))
+@pytest.mark.parametrize("mode", range(11))
 def test_gather_probe_reads_every_selected_row(dsa, dev, mode):
     """The gather probe (measurement helper) reads each valid selected 1152-byte
     row exactly once per query: the XOR of its per-wave checksums equals the XOR
