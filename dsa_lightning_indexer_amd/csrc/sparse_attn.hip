@@ -465,20 +465,32 @@ __global__ __launch_bounds__(256, 1) void sa_mla1_kernel(SAParams p, int64_t row
   // soon as all fragments are in registers -- measured slower: 25.1 and 29.4 ms
   // against 24.5 ms on the C4 layer.)
   auto step = [&](const uint8_t* tile, uint64_t vm, auto&& refill) {
+    // K fragments four ahead of their MFMAs (a ring of four registers sets)
+    auto kaddr = [&](int ks) { return ks < KSV ? tile + fv + 64 * ks : tile + (ks == KSV ? fr0 : fr1); };
     f32x4 a0 = f32x4{}, a1 = f32x4{};
+    bf16x8 kr[4];
 #pragma unroll
-    for (int ks = 0; ks < KSV; ks += 2) {
-      const bf16x8 k0 = *(const bf16x8*)(tile + fv + 64 * ks);
-      const bf16x8 k1 = *(const bf16x8*)(tile + fv + 64 * (ks + 1));
-      a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[ks], a0, 0, 0, 0);
-      a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[ks + 1], a1, 0, 0, 0);
+    for (int ks = 0; ks < 4; ++ks) kr[ks] = *(const bf16x8*)kaddr(ks);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 kc = kr[ks & 3];
+      if (ks + 4 < KS) kr[ks & 3] = *(const bf16x8*)kaddr(ks + 4);
+      if (ks & 1) a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc, qf[ks], a1, 0, 0, 0);
+      else a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc, qf[ks], a0, 0, 0, 0);
     }
-    {
-      const bf16x8 k0 = *(const bf16x8*)(tile + fr0);
-      const bf16x8 k1 = *(const bf16x8*)(tile + fr1);
-      a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[KSV], a0, 0, 0, 0);
-      a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[KSV + 1], a1, 0, 0, 0);
+    // keep four K-fragment reads in flight ahead of the MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS - 4; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    // the first eight V fragments are read while the softmax runs
+    auto vread = [&](int dt) { return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tile + fvt + 32 * dt)); };
+    bf16x4 va[2][8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) va[0][d] = vread(d);
     const f32x4 sc = a0 + a1;
     const uint32_t vb = (uint32_t)(vm >> (4 * g));
     float z[4];
@@ -500,19 +512,24 @@ __global__ __launch_bounds__(256, 1) void sa_mla1_kernel(SAParams p, int64_t row
     bf16x4 pb_hi, pb_lo;
     split_bf16(pe, pb_hi, pb_lo);
     l_run += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+    // eight output tiles at a time (the hi and lo products of one tile eight
+    // MFMAs apart), the next eight V fragments read before this group's MFMAs
 #pragma unroll
-    for (int d0 = 0; d0 < NDT; d0 += 8) {
-      bf16x4 va[8];
+    for (int q = 0; q < NDT / 8; ++q) {
+      if (q + 1 < NDT / 8) {
 #pragma unroll
-      for (int d = 0; d < 8; ++d)
-        va[d] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tile + fvt + 32 * (d0 + d)));
+        for (int d = 0; d < 8; ++d) va[(q + 1) & 1][d] = vread(8 * (q + 1) + d);
+      } else {
+        // the last group's fragments are the tile's last reads: refill once
+        // they have returned, before its MFMAs
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        refill();
+      }
 #pragma unroll
-      for (int d = 0; d < 8; ++d) o[d0 + d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[d], pb_hi, o[d0 + d], 0, 0, 0);
+      for (int d = 0; d < 8; ++d) o[8 * q + d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[q & 1][d], pb_hi, o[8 * q + d], 0, 0, 0);
 #pragma unroll
-      for (int d = 0; d < 8; ++d) o[d0 + d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[d], pb_lo, o[d0 + d], 0, 0, 0);
+      for (int d = 0; d < 8; ++d) o[8 * q + d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[q & 1][d], pb_lo, o[8 * q + d], 0, 0, 0);
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    refill();
   };
 
   idx_dma(0);
