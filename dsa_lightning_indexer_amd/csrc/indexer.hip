@@ -987,8 +987,8 @@ __device__ __forceinline__ void tile_scores2(const Row2<DT>& rs, const uint8_t* 
 #pragma unroll
   for (int t = 0; t < NS - 1; ++t) {
     mfma_row2<DT>(rs.a[1], bf, acc1);              // row 1, step t
+    load_bf2<DT>(kt, t + 1, g, col, bf);           // (its latency hidden by row 0's sum)
     p0[t] = epi_row2(acc0, w2[0], g);              // row 0, step t (under row 1's MFMAs)
-    load_bf2<DT>(kt, t + 1, g, col, bf);
     mfma_row2<DT>(rs.a[0], bf, acc0);              // row 0, step t + 1
     p1[t] = epi_row2(acc1, w2[1], g);              // row 1, step t (under row 0's MFMAs)
   }
