@@ -82,6 +82,19 @@ def test_mla_invalid_entries_and_empty_rows(dsa, dev, n):
     assert (got[0, 10] == 0).all() and (got[0, 11] == 0).all()
 
 
+@pytest.mark.parametrize("topk", [1, 17, 100, 700])
+def test_mla_rows_kernel_short_index_rows(dsa, dev, topk):
+    """The one-wave-per-row kernel (from 1024 rows) on index rows of other
+    lengths than 2048: a row ending inside a 16-position step and inside a
+    64-entry block of the index ring; 1030 rows leave the last workgroup two
+    rows."""
+    n = 1030
+    sa = syn.sa_inputs(n_q=n, n_k=n, seed=13, device=dev)
+    idx = syn.random_sorted_indices(n_q=n, topk=topk, seed=14, device=dev)
+    rows = np.array(sorted(set([0, 1, topk - 1, topk, 511, 1000, n - 2, n - 1])))
+    check_sa(dsa, sa, idx, rows)
+
+
 @pytest.mark.parametrize("latent,kv_heads,dtype", [(False, 2, syn.BF16), (True, 4, syn.BF16), (False, 1, syn.F32)])
 def test_generic_paths(dsa, dev, latent, kv_heads, dtype):
     n = 200
