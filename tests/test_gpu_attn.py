@@ -95,6 +95,16 @@ def test_mla_rows_kernel_short_index_rows(dsa, dev, topk):
     check_sa(dsa, sa, idx, rows)
 
 
+def test_mla_rows_kernel_batched(dsa, dev):
+    """Two batches of 600 query rows (1200 rows: the one-wave-per-row kernel),
+    queries at positions 100..699 of a 700-row latent cache per batch: each
+    row gathers from its own batch's rows."""
+    B, n_q, n_k = 2, 600, 700
+    sa = syn.sa_inputs(B=B, n_q=n_q, n_k=n_k, seed=15, device=dev)
+    idx = syn.random_sorted_indices(B=B, n_q=n_q, topk=2048, q_pos0=n_k - n_q, n_k=n_k, seed=16, device=dev)
+    check_sa(dsa, sa, idx, np.array([0, 1, 299, 598, 599]))
+
+
 @pytest.mark.parametrize("latent,kv_heads,dtype", [(False, 2, syn.BF16), (True, 4, syn.BF16), (False, 1, syn.F32)])
 def test_generic_paths(dsa, dev, latent, kv_heads, dtype):
     n = 200
