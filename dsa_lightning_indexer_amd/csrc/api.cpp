@@ -271,7 +271,8 @@ dsa_status dsa_topk(const dsa_indexer_args* a, const float* scores, int32_t k, i
 }
 
 size_t dsa_sparse_attn_workspace_size(const dsa_sparse_attn_args* a) {
-  if (!a || check_sa(a, false) != DSA_OK) return 0;
+  // (the size depends on the shapes only: idx and out may still be NULL)
+  if (!a || check_sa(a, false, false) != DSA_OK) return 0;
   return align_up(dsa_host::sparse_attn_ws_bytes(*a));
 }
 

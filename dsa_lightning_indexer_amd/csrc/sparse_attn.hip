@@ -83,7 +83,11 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Weights p (4 per lane) as bf16 hi + lo parts: hi = bf16(p), lo = bf16(p - hi),
-// converted two at a time.
+// converted two at a time.  The P.V products take both parts in one
+// v_mfma_f32_16x16x32_bf16 per output tile: a lane's eight K slots hold hi and
+// then lo of its four positions, against its V fragment of those positions
+// twice.  (Two 16x16x16 products give the same sum, but that form runs at half
+// the 16x16x32 form's rate on gfx950.)
 __device__ __forceinline__ void split_bf16(const float (&pe)[4], bf16x4& hi, bf16x4& lo) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -307,12 +311,13 @@ __global__ __launch_bounds__(256, 3) void sa_mla4_kernel(SAParams p) {
     for (int i = 0; i < 4; ++i) pe[i] = __builtin_amdgcn_exp2f(z[i] - mref);
     bf16x4 pb_hi, pb_lo;
     split_bf16(pe, pb_hi, pb_lo);
+    const bf16x8 pb2 = __builtin_shufflevector(pb_hi, pb_lo, 0, 1, 2, 3, 4, 5, 6, 7);
     l_run += (pe[0] + pe[1]) + (pe[2] + pe[3]);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(rbase + 32 * dt));
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_hi, o[dt], 0, 0, 0);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_lo, o[dt], 0, 0, 0);
+      const bf16x8 v2 = __builtin_shufflevector(va, va, 0, 1, 2, 3, 0, 1, 2, 3);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v2, pb2, o[dt], 0, 0, 0);
     }
     // this wave's V tile is rewritten next step only after these reads returned
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -511,9 +516,10 @@ __global__ __launch_bounds__(256, 1) void sa_mla1_kernel(SAParams p, int64_t row
     for (int i = 0; i < 4; ++i) pe[i] = __builtin_amdgcn_exp2f(z[i] - mref);
     bf16x4 pb_hi, pb_lo;
     split_bf16(pe, pb_hi, pb_lo);
+    const bf16x8 pb2 = __builtin_shufflevector(pb_hi, pb_lo, 0, 1, 2, 3, 4, 5, 6, 7);
     l_run += (pe[0] + pe[1]) + (pe[2] + pe[3]);
-    // eight output tiles at a time (the hi and lo products of one tile eight
-    // MFMAs apart), the next eight V fragments read before this group's MFMAs
+    // eight output tiles at a time, the next eight V fragments read before this
+    // group's MFMAs
 #pragma unroll
     for (int q = 0; q < NDT / 8; ++q) {
       if (q + 1 < NDT / 8) {
@@ -526,9 +532,10 @@ __global__ __launch_bounds__(256, 1) void sa_mla1_kernel(SAParams p, int64_t row
         refill();
       }
 #pragma unroll
-      for (int d = 0; d < 8; ++d) o[8 * q + d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[q & 1][d], pb_hi, o[8 * q + d], 0, 0, 0);
-#pragma unroll
-      for (int d = 0; d < 8; ++d) o[8 * q + d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[q & 1][d], pb_lo, o[8 * q + d], 0, 0, 0);
+      for (int d = 0; d < 8; ++d) {
+        const bf16x8 v2 = __builtin_shufflevector(va[q & 1][d], va[q & 1][d], 0, 1, 2, 3, 0, 1, 2, 3);
+        o[8 * q + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v2, pb2, o[8 * q + d], 0, 0, 0);
+      }
     }
   };
 

@@ -74,6 +74,13 @@ static void check_attention(void) {
   dsa_sparse_attn_args a = sa(8, 1, 204800, 2048);
   EXPECT(dsa_sparse_attn_workspace_size(&a) > 0);
   EXPECT(dsa_sparse_attn(&a, NULL, 0, NULL) == DSA_ERR_WORKSPACE);
+  {
+    /* the size query reads the shapes only */
+    dsa_sparse_attn_args b = a;
+    b.idx = NULL;
+    b.out = NULL;
+    EXPECT(dsa_sparse_attn_workspace_size(&b) == dsa_sparse_attn_workspace_size(&a));
+  }
   a.topk = 0;
   EXPECT(dsa_sparse_attn(&a, NULL, 0, NULL) == DSA_ERR_INVALID);
   a = sa(1, 4, 100, 16);

@@ -118,6 +118,19 @@ def test_sparse_attn_decode_needs_workspace():
     need = L.dsa_sparse_attn_workspace_size(ctypes.byref(a))
     assert need > 0
     assert L.dsa_sparse_attn(ctypes.byref(a), None, 0, None) == 3
+    # the size query needs only the shapes: no idx or output yet
+    assert L.dsa_sparse_attn_workspace_size(ctypes.byref(sa(batch=8, n_q=1, n_k=204800, idx=None, out=None))) == need
+
+
+def test_sparse_attn_workspace_size_binding():
+    # the Python query (no output tensor) agrees with what the launch asks for
+    import torch
+    from dsa_lightning_indexer_amd import api
+    q = torch.empty((8, 1, 16, 576), dtype=torch.bfloat16)
+    kv = torch.empty((8, 204800, 1, 576), dtype=torch.bfloat16)
+    idx = torch.empty((8, 1, 2048), dtype=torch.int32)
+    need = L.dsa_sparse_attn_workspace_size(ctypes.byref(sa(batch=8, n_q=1, n_k=204800)))
+    assert api.sparse_attn_workspace_size(q, kv, idx, 512) == need > 0
 
 
 def layers(pattern, null_s=True):
