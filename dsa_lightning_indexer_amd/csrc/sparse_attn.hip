@@ -574,37 +574,42 @@ __global__ __launch_bounds__(256, 1) void sa_mla1_kernel(SAParams p, int64_t row
   for (int dt = 0; dt < NDT; ++dt) __builtin_nontemporal_store(o[dt] * inv, (f32x4*)(out + 16 * dt));
 }
 
-// Merge the split partials of one (query row, head): thread c loads column c of
-// every split's partial output first (all loads in flight at once), while wave
-// 0 forms the weights exp(m_s - M) in LDS; then each thread sums its column.
+// Merge the split partials of one (query row, head) over 256 of its output
+// columns: one wave, lane c holds columns 4c .. 4c + 3.  Every split's partial
+// is loaded first (all loads in flight at once), then the lanes below nsplit
+// form the weights exp(m_s - M) and the wave reads them back one split at a
+// time.
 constexpr int kMaxSplit = kMaxTopk / 64;    // splits hold at least 64 positions
-__global__ __launch_bounds__(512) void sa_combine_kernel(SAParams p) {
-  __shared__ float wsum[2];
-  __shared__ float wgt[kMaxSplit];
-  const int h = blockIdx.x % p.heads;
-  const int64_t gi = blockIdx.x / p.heads;
+constexpr int kCombineCols = 256;           // output columns per combine wave
+__global__ __launch_bounds__(64) void sa_combine_kernel(SAParams p) {
+  const int parts = p.d_v / kCombineCols;
+  const int part = (int)(blockIdx.x % parts);
+  const int64_t rh = blockIdx.x / parts;     // (query row, head)
+  const int h = (int)(rh % p.heads);
+  const int64_t gi = rh / p.heads;
+  const int lane = threadIdx.x;
   const float* ml = p.ws_ml + (gi * p.nsplit * p.heads + h) * 2;   // split stride: heads * 2
-  const float* po = p.ws_o + (gi * p.nsplit * p.heads + h) * (int64_t)p.d_v;
+  const float* po = p.ws_o + (gi * p.nsplit * p.heads + h) * (int64_t)p.d_v + kCombineCols * part + 4 * lane;
   const int64_t sstride = (int64_t)p.heads * p.d_v;
-  const int c = threadIdx.x;                 // one output column per thread (d_v = blockDim.x)
-  float v[kMaxSplit];
+  f32x4 v[kMaxSplit];
 #pragma unroll
-  for (int sp = 0; sp < kMaxSplit; ++sp) v[sp] = sp < p.nsplit ? po[sp * sstride + c] : 0.f;
-  if (threadIdx.x < 64) {
-    const float ms = (int)threadIdx.x < p.nsplit ? ml[(int64_t)threadIdx.x * p.heads * 2] : -__builtin_inff();
-    const float ls = (int)threadIdx.x < p.nsplit ? ml[(int64_t)threadIdx.x * p.heads * 2 + 1] : 0.f;
-    const float M = wave_max(ms);
-    const float w = (ms == -__builtin_inff()) ? 0.f : __expf(ms - M);
-    if ((int)threadIdx.x < kMaxSplit) wgt[threadIdx.x] = w;
-    const float L = wave_sum(w * ls);
-    if (threadIdx.x == 0) wsum[0] = L > 0.f ? 1.f / L : 0.f;
+  for (int sp = 0; sp < kMaxSplit; ++sp) v[sp] = sp < p.nsplit ? *(const f32x4*)(po + sp * sstride) : f32x4{};
+  const float ms = lane < p.nsplit ? ml[(int64_t)lane * p.heads * 2] : -__builtin_inff();
+  const float ls = lane < p.nsplit ? ml[(int64_t)lane * p.heads * 2 + 1] : 0.f;
+  const float M = wave_max(ms);
+  const float w = (ms == -__builtin_inff()) ? 0.f : __expf(ms - M);
+  const float L = wave_sum(w * ls);
+  f32x4 acc = f32x4{};
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplit; ++sp) {
+    if (sp < p.nsplit) {
+      const float wsp = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), sp));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(wsp, v[sp][i], acc[i]);
+    }
   }
-  __syncthreads();
-  float acc = 0.f;
-#pragma unroll
-  for (int sp = 0; sp < kMaxSplit; ++sp)
-    if (sp < p.nsplit) acc = fmaf(wgt[sp], v[sp], acc);
-  p.out[(gi * p.heads + h) * (int64_t)p.d_v + c] = acc * wsum[0];
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  *(f32x4*)(p.out + (gi * p.heads + h) * (int64_t)p.d_v + kCombineCols * part + 4 * lane) = acc * inv;
 }
 
 bool mla_ok(const dsa_sparse_attn_args& a) {
@@ -668,7 +673,8 @@ hipError_t sparse_attn_launch(const dsa_sparse_attn_args& a, void* ws, hipStream
     dim3 grid((unsigned)(rows * p.nsplit));
     hipLaunchKernelGGL((sa_mla4_kernel<576, 512>), grid, dim3(256), 0, s, p);
     if (p.nsplit > 1) {
-      hipLaunchKernelGGL(sa_combine_kernel, dim3((unsigned)(rows * a.heads)), dim3(512), 0, s, p);
+      hipLaunchKernelGGL(sa_combine_kernel, dim3((unsigned)(rows * a.heads * (a.d_v / kCombineCols))), dim3(64), 0,
+                         s, p);
     }
     return hipGetLastError();
   }
