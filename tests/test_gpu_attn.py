@@ -65,6 +65,18 @@ def test_mla_decode_split(dsa, dev):
     check_sa(dsa, sa, idx)
 
 
+@pytest.mark.parametrize("B,topk", [(5, 1000), (1, 700), (8, 130), (2, 100)])
+def test_mla_decode_ragged_splits(dsa, dev, B, topk):
+    """Decode shapes whose index rows split unevenly: 1000 entries over 15
+    splits of 67 (the last 62), 700 over 10 of 70, 130 over 2 of 65; 100
+    entries give a single split (no combine).  Splits end inside 16-position
+    steps."""
+    S = 5000
+    sa = syn.sa_inputs(B=B, n_q=1, n_k=S, seed=21, device=dev)
+    idx = syn.random_sorted_indices(B=B, n_q=1, topk=topk, q_pos0=S - 1, seed=22, device=dev)
+    check_sa(dsa, sa, idx)
+
+
 @pytest.mark.parametrize("n", [300, 1103])
 def test_mla_invalid_entries_and_empty_rows(dsa, dev, n):
     """Empty rows, out-of-range entries and ragged row counts.  300 rows run the
