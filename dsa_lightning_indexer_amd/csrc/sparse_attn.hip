@@ -12,14 +12,16 @@
 //                                                the gathered rows, partials
 //                                                are summed through LDS)
 //      online softmax per head (the S^T layout gives each lane one head)
-//      O^T[128 x 16] += V_sel^T . P^T          (16x16x16 bf16 MFMA per wave on
-//                                                its 128 V columns; V^T comes
-//                                                from the gathered rows via a
-//                                                transposing LDS read)
+//      O^T[128 x 16] += V_sel^T . P^T          (16x16x32 bf16 MFMA per wave on
+//                                                its 128 V columns, P in bf16
+//                                                hi and lo parts along K; V^T
+//                                                comes from the gathered rows
+//                                                via a transposing LDS read)
 //    P^T needs no data movement: the S^T accumulator layout (lane = head,
-//    registers = 4 consecutive keys) is exactly the B-operand layout of the
-//    16x16x16 MFMA.  With several splits per row the partial (max, sum, O) go
-//    to the workspace and sa_combine_kernel merges them.  Used below 1024 rows
+//    registers = 4 consecutive keys) is the B-operand layout of a 16-deep
+//    MFMA, and its hi and lo parts side by side that of the 32-deep one.
+//    With several splits per row the partial (max, sum, O) go to the
+//    workspace and sa_combine_kernel merges them.  Used below 1024 rows
 //    (decode), where rows are split to fill the chip.
 //  * sa_mla1_kernel     the same arithmetic with one wave per query row (from
 //    1024 rows, no splits): the wave gathers whole latent rows straight into
